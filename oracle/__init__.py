@@ -1,0 +1,16 @@
+"""fp64 CPU oracle (test infrastructure only; never on the product path)."""
+
+from .tpmlp_oracle import (  # noqa: F401
+    GELU_CUBIC,
+    LN_EPS,
+    SQRT_2_OVER_PI,
+    gelu,
+    gelu_scalar,
+    layer_norm,
+    layer_norm_loops,
+    post_ln_ffn,
+    shard_mlp,
+    shard_outputs,
+    tp_mlp,
+    tp_mlp_loops,
+)
