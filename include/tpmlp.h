@@ -1,0 +1,205 @@
+/*
+ * tpmlp.h -- C ABI of the MI355X (gfx950) tensor-parallel MLP library.
+ *
+ * The library computes the Megatron tensor-parallel MLP forward pass
+ *
+ *     Y = sum_{i<n} GeLU_tanh(X A_i) B_i
+ *
+ * where A (D x F) is split by columns into n contiguous blocks A_i and B
+ * (F x D) by the matching rows into B_i.  The operations and their names
+ * follow "Tensor-Parallel MLP (Megatron)" (scratchllm.com), section
+ * "What to implement": gelu(x), shard_mlp(A, B, n) and tp_mlp(X, shards).
+ * The n partial outputs are summed on the GPU inside one fp32 accumulator
+ * (the simulated all-reduce of section "The split", bullet 3).
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are dense, row-major, with no padding between rows.
+ *   - Every data pointer is a device pointer on the current HIP device,
+ *     16-byte aligned.  The caller allocates and owns all device memory
+ *     (inputs, outputs, the packed weight buffer and the workspace); the
+ *     library never allocates device memory.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Work is enqueued asynchronously on it; the caller
+ *     synchronises.  Faults inside a kernel surface at that synchronisation,
+ *     not as a return value.
+ *   - Every function returns a tpmlp_status (or a size / count).  Arguments
+ *     are validated before any HIP call, so argument errors are reported
+ *     without touching the GPU.  No C++ exception crosses this boundary and
+ *     nothing aborts.
+ *   - dtype: TPMLP_F32 (IEEE binary32) or TPMLP_BF16 (bfloat16).  Products
+ *     always accumulate in fp32.
+ *   - Calls on different streams may overlap only when they use different
+ *     workspaces.
+ */
+#ifndef TPMLP_H
+#define TPMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TPMLP_F32 = 0,
+    TPMLP_BF16 = 1
+} tpmlp_dtype;
+
+typedef enum {
+    TPMLP_OK = 0,
+    TPMLP_ERR_NULL = 1,          /* a required pointer is NULL                         */
+    TPMLP_ERR_SHAPE = 2,         /* a size is out of range (negative, zero where a
+                                    positive size is required, n > F, shard index
+                                    outside [0, n), or too large for the kernels)    */
+    TPMLP_ERR_INDIVISIBLE = 3,   /* F is not divisible by n                            */
+    TPMLP_ERR_DTYPE = 4,         /* unknown dtype or a dtype combination not offered   */
+    TPMLP_ERR_WORKSPACE = 5,     /* packed buffer or workspace missing or too small    */
+    TPMLP_ERR_ALIGN = 6,         /* a device pointer is not 16-byte aligned            */
+    TPMLP_ERR_HIP = 7            /* the HIP runtime reported an error                  */
+} tpmlp_status;
+
+/* Opaque host-side descriptor of a sharded weight set: D, F, n, dtype and the
+ * device address of the packed weights.  Created by tpmlp_shard, freed by
+ * tpmlp_shards_destroy.  Immutable after creation except for the workspace
+ * bound with tpmlp_set_workspace. */
+typedef struct tpmlp_shards tpmlp_shards;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* tpmlp_status_string(int status);
+
+/* Library version string, e.g. "tpmlp 0.1 gfx950". */
+const char* tpmlp_version(void);
+
+/*
+ * tpmlp_gelu -- y[k] = GeLU_tanh(x[k]) for k < count.
+ * "Tensor-Parallel MLP (Megatron)", section "GeLU": one half of x times
+ * (1 + tanh u) with u = sqrt(2/pi) (x + 0.044715 x^3), entry by entry.
+ *   x, y   device arrays of `count` elements of `dtype`; x == y (in place) is
+ *          allowed, other overlaps are not.
+ *   count  number of elements; 0 is a no-op, negative is TPMLP_ERR_SHAPE.
+ * Evaluated in fp32 (bf16 inputs are widened, the result rounded to nearest
+ * even).
+ */
+tpmlp_status tpmlp_gelu(const void* x, void* y, int64_t count, int dtype, void* stream);
+
+/*
+ * Bytes of the packed weight buffer tpmlp_shard needs for (D, F, n, dtype);
+ * 0 if the arguments are invalid.
+ */
+size_t tpmlp_shard_bytes(int64_t D, int64_t F, int n, int dtype);
+
+/*
+ * tpmlp_shard -- split A and B into n pairs (A_i, B_i) and pack them.
+ * "Tensor-Parallel MLP (Megatron)", sections "The split" and "Requirements":
+ * pair i holds columns iF/n .. (i+1)F/n - 1 of A and the same range of
+ * rows of B; F must be divisible by n ("What to implement").
+ *   A       device, D x F row-major, `dtype`.
+ *   B       device, F x D row-major, `dtype`.
+ *   packed  device buffer of at least tpmlp_shard_bytes(D, F, n, dtype)
+ *           bytes, owned by the caller, which must keep it alive and
+ *           unmodified while the returned descriptor is in use.  The pairs are
+ *           stored K-contiguous for the matrix cores (A_i transposed to
+ *           F/n x D, B transposed to D x F); A and B may be released once the
+ *           work enqueued on `stream` has completed.
+ *   out     receives a new host descriptor (set to NULL on error).
+ * Errors: TPMLP_ERR_NULL, TPMLP_ERR_SHAPE (D <= 0, F <= 0, n <= 0, n > F,
+ * a dimension above 2^21), TPMLP_ERR_INDIVISIBLE
+ * (F % n != 0), TPMLP_ERR_DTYPE, TPMLP_ERR_WORKSPACE (packed_bytes too
+ * small), TPMLP_ERR_ALIGN, TPMLP_ERR_HIP.
+ */
+tpmlp_status tpmlp_shard(const void* A, const void* B, int64_t D, int64_t F, int n, int dtype,
+                         void* packed, size_t packed_bytes, tpmlp_shards** out, void* stream);
+
+/* Number of shards n of a descriptor (0 if s is NULL). */
+int tpmlp_shard_count(const tpmlp_shards* s);
+
+/* Sizes of a descriptor; any output pointer may be NULL. */
+tpmlp_status tpmlp_shard_info(const tpmlp_shards* s, int64_t* D, int64_t* F, int* n, int* dtype);
+
+/*
+ * tpmlp_shard_unpack -- write pair i back in the page's layout:
+ * A_i (D x F/n row-major) and B_i (F/n x D row-major), both `dtype`, device.
+ * Either output may be NULL to skip it.  Bit-exact copy of the inputs given
+ * to tpmlp_shard.  Errors: TPMLP_ERR_NULL (s), TPMLP_ERR_SHAPE (i outside
+ * [0, n)), TPMLP_ERR_ALIGN, TPMLP_ERR_HIP.
+ */
+tpmlp_status tpmlp_shard_unpack(const tpmlp_shards* s, int i, void* A_i, void* B_i, void* stream);
+
+/* Frees the host descriptor only; the packed buffer belongs to the caller. */
+void tpmlp_shards_destroy(tpmlp_shards* s);
+
+/* Option flags for the forward workspace size and tpmlp_forward_ex. */
+enum {
+    TPMLP_OPT_LAYERNORM = 1      /* normalise each row of X first (no affine)  */
+};
+
+/*
+ * Bytes of device workspace a forward pass over M rows needs: the
+ * intermediate H = GeLU(X A_i) for every shard (M x F, or M x F/n for a
+ * single shard, in the weights' dtype) plus, with TPMLP_OPT_LAYERNORM, two
+ * fp32 per-row statistics.  Returns 0 for invalid arguments.
+ * `single_shard` != 0 sizes it for a forward restricted to one shard.
+ */
+size_t tpmlp_forward_workspace_bytes(const tpmlp_shards* s, int64_t M, int flags, int single_shard);
+
+/*
+ * Bind a caller-owned device workspace to the descriptor for tpmlp_forward.
+ * ws may be NULL with bytes 0 to unbind.  Errors: TPMLP_ERR_NULL (s),
+ * TPMLP_ERR_ALIGN.
+ */
+tpmlp_status tpmlp_set_workspace(tpmlp_shards* s, void* ws, size_t bytes);
+
+/*
+ * tpmlp_forward -- Y = sum_i GeLU_tanh(X A_i) B_i.
+ * "Tensor-Parallel MLP (Megatron)", section "The split": each shard's
+ * intermediate H_i = GeLU(X A_i) (bullet 1), its partial Y_i = H_i B_i of
+ * the full output shape (bullet 2), and the sum of the partials (bullet 3);
+ * "Requirements": the result equals the unsplit GeLU(X A) B.
+ *   X   device, M x D row-major, the descriptor's dtype.
+ *   M   number of token rows; 0 is a no-op, negative is TPMLP_ERR_SHAPE.
+ *   s   descriptor from tpmlp_shard with a workspace of at least
+ *       tpmlp_forward_workspace_bytes(s, M, 0, 0) bytes bound.
+ *   Y   device, M x D row-major, the descriptor's dtype; must not overlap X.
+ * The shard sum is formed in one fp32 accumulator per output element and
+ * rounded once to Y's dtype.
+ */
+tpmlp_status tpmlp_forward(const void* X, int64_t M, const tpmlp_shards* s, void* Y, void* stream);
+
+/* Options of tpmlp_forward_ex.  Zero-initialise, then set what is needed. */
+typedef struct {
+    int flags;                 /* TPMLP_OPT_LAYERNORM or 0                                  */
+    float ln_eps;              /* LayerNorm epsilon; 0 selects 1e-5                         */
+    int y_dtype;               /* output dtype; -1 selects the descriptor's dtype            */
+    const void* residual;      /* optional M x D, X's dtype: added once after the shard sum  */
+    int shard_index;           /* -1: all shards (the sum); i in [0, n): partial Y_i only    */
+    void* workspace;           /* optional: overrides the bound workspace                    */
+    size_t workspace_bytes;
+    void* const* events;       /* optional: 4 hipEvent_t recorded on the stream before the
+                                  LayerNorm statistics, before the first GEMM, between the
+                                  GEMMs and after the second GEMM (NULL entries skipped)      */
+} tpmlp_opts;
+
+/* Fills *o with the defaults described above. */
+void tpmlp_opts_init(tpmlp_opts* o);
+
+/*
+ * tpmlp_forward_ex -- tpmlp_forward with options.
+ * With TPMLP_OPT_LAYERNORM and a residual this is the FFN half of the Post-LN
+ * block of "LLM Lab Notes 06: Building a Megatron-Style Transformer Block
+ * from Scratch", section 2, markers 5 to 7: out = x + TP-MLP(LayerNorm(x)),
+ * LayerNorm over each row without affine parameters (mean and biased
+ * variance in fp32), the residual x un-normalised and added once.
+ * shard_index = i returns only GPU i's partial Y_i of section "The split",
+ * bullet 2 (with a residual, the residual is added to that partial).
+ * y_dtype may be TPMLP_F32 for bf16 weights (fp32 output); a bf16 output for
+ * fp32 weights is TPMLP_ERR_DTYPE.
+ */
+tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, void* Y,
+                              const tpmlp_opts* opts, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPMLP_H */

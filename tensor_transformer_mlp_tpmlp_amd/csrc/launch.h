@@ -1,0 +1,51 @@
+// Host-side launchers of the tpmlp kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+constexpr int kEpiGelu = 0;   // C = GeLU_tanh(acc), rounded to C's dtype
+constexpr int kEpiStore = 1;  // C = acc (+ R), rounded to C's dtype
+
+// C[m][n] = epi( sum_k a(m,k) * Bop[n][k] ), m < M, n < N, k < K, where
+// a(m,k) = Aop[m][k], or (Aop[m][k] - ln_mean[m]) * ln_rstd[m] when ln_mean
+// is given.  Aop is M x K row-major (lda), Bop is N x K row-major (ldb): both
+// operands are K-contiguous.  Aop, Bop and R have dtype ab_dtype; C has
+// c_dtype.  Products accumulate in fp32.
+struct GemmArgs {
+    const void* A = nullptr;
+    int64_t lda = 0;
+    const void* B = nullptr;
+    int64_t ldb = 0;
+    int64_t M = 0, N = 0, K = 0;
+    void* C = nullptr;
+    int64_t ldc = 0;
+    int c_dtype = kBF16;
+    const void* R = nullptr;  // optional residual, M x N, ab_dtype
+    int64_t ldr = 0;
+    const float* ln_mean = nullptr;
+    const float* ln_rstd = nullptr;
+    int epi = kEpiStore;
+    int ab_dtype = kBF16;
+};
+
+// Which kernel family a GEMM goes to.
+enum GemmPath { kPathFastBf16 = 0, kPathGeneric = 1 };
+GemmPath choose_gemm_path(const GemmArgs& g);
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemm_generic(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemm_bf16_fast(const GemmArgs& g, hipStream_t stream);
+
+hipError_t launch_gelu(const void* x, void* y, int64_t count, int dtype, hipStream_t stream);
+hipError_t launch_ln_stats(const void* x, int64_t M, int64_t D, int dtype, float eps, float* mean,
+                           float* rstd, hipStream_t stream);
+hipError_t launch_transpose(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
+                            int elem_bytes, hipStream_t stream);
+
+}  // namespace tpmlp

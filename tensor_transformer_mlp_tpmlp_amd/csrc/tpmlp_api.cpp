@@ -1,0 +1,275 @@
+// C ABI of the tpmlp library: argument validation, the shard descriptor,
+// workspace layout and kernel dispatch.  Every check runs before the first
+// HIP call so argument errors never reach the GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/tpmlp.h"
+#include "launch.h"
+
+using namespace tpmlp;
+
+struct tpmlp_shards {
+    int64_t D;
+    int64_t F;
+    int n;
+    int dtype;
+    void* packed;        // A^T (F x D) followed by B^T (D x F), both `dtype`
+    size_t packed_bytes;
+    void* ws;            // bound workspace (caller-owned)
+    size_t ws_bytes;
+};
+
+namespace {
+
+// Largest size of a single dimension (rows or columns) accepted: keeps every
+// grid dimension and every 32-bit in-tile offset of the kernels in range.
+constexpr int64_t kMaxDim = (int64_t)1 << 21;
+constexpr size_t kAlign = 256;
+
+size_t elem_size(int dtype) { return dtype == TPMLP_F32 ? 4 : 2; }
+bool valid_dtype(int dtype) { return dtype == TPMLP_F32 || dtype == TPMLP_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+tpmlp_status from_hip(hipError_t e) { return e == hipSuccess ? TPMLP_OK : TPMLP_ERR_HIP; }
+
+tpmlp_status check_shard_args(int64_t D, int64_t F, int n, int dtype) {
+    if (!valid_dtype(dtype)) return TPMLP_ERR_DTYPE;
+    if (D <= 0 || F <= 0 || n <= 0 || D > kMaxDim || F > kMaxDim) return TPMLP_ERR_SHAPE;
+    if (n > F) return TPMLP_ERR_SHAPE;
+    if (F % n != 0) return TPMLP_ERR_INDIVISIBLE;
+    return TPMLP_OK;
+}
+
+// Workspace layout for a forward over M rows with N_h intermediate columns:
+//   [H: M x N_h, weights' dtype][mean: M fp32][rstd: M fp32], each segment
+//   256-byte aligned.
+struct WsLayout {
+    size_t h_off, mean_off, rstd_off, total;
+};
+
+WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard) {
+    const int64_t nh = single_shard ? s->F / s->n : s->F;
+    WsLayout L;
+    L.h_off = 0;
+    size_t off = round_up((size_t)M * (size_t)nh * elem_size(s->dtype));
+    L.mean_off = L.rstd_off = off;
+    if (flags & TPMLP_OPT_LAYERNORM) {
+        L.mean_off = off;
+        off += round_up((size_t)M * 4);
+        L.rstd_off = off;
+        off += round_up((size_t)M * 4);
+    }
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tpmlp_status_string(int status) {
+    switch (status) {
+        case TPMLP_OK: return "TPMLP_OK";
+        case TPMLP_ERR_NULL: return "TPMLP_ERR_NULL: a required pointer is NULL";
+        case TPMLP_ERR_SHAPE: return "TPMLP_ERR_SHAPE: a size is out of range";
+        case TPMLP_ERR_INDIVISIBLE: return "TPMLP_ERR_INDIVISIBLE: F is not divisible by n";
+        case TPMLP_ERR_DTYPE: return "TPMLP_ERR_DTYPE: unsupported dtype";
+        case TPMLP_ERR_WORKSPACE: return "TPMLP_ERR_WORKSPACE: buffer missing or too small";
+        case TPMLP_ERR_ALIGN: return "TPMLP_ERR_ALIGN: device pointer not 16-byte aligned";
+        case TPMLP_ERR_HIP: return "TPMLP_ERR_HIP: HIP runtime error";
+        default: return "TPMLP_ERR_UNKNOWN";
+    }
+}
+
+const char* tpmlp_version(void) { return "tpmlp 0.1 gfx950"; }
+
+tpmlp_status tpmlp_gelu(const void* x, void* y, int64_t count, int dtype, void* stream) {
+    if (!valid_dtype(dtype)) return TPMLP_ERR_DTYPE;
+    if (count < 0) return TPMLP_ERR_SHAPE;
+    if (count == 0) return TPMLP_OK;
+    if (!x || !y) return TPMLP_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y)) return TPMLP_ERR_ALIGN;
+    return from_hip(launch_gelu(x, y, count, dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t tpmlp_shard_bytes(int64_t D, int64_t F, int n, int dtype) {
+    if (check_shard_args(D, F, n, dtype) != TPMLP_OK) return 0;
+    return round_up((size_t)D * (size_t)F * elem_size(dtype)) * 2;
+}
+
+tpmlp_status tpmlp_shard(const void* A, const void* B, int64_t D, int64_t F, int n, int dtype,
+                         void* packed, size_t packed_bytes, tpmlp_shards** out, void* stream) {
+    if (out) *out = nullptr;
+    if (!A || !B || !packed || !out) return TPMLP_ERR_NULL;
+    tpmlp_status st = check_shard_args(D, F, n, dtype);
+    if (st != TPMLP_OK) return st;
+    if (packed_bytes < tpmlp_shard_bytes(D, F, n, dtype)) return TPMLP_ERR_WORKSPACE;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(packed)) return TPMLP_ERR_ALIGN;
+
+    tpmlp_shards* s = new (std::nothrow) tpmlp_shards;
+    if (!s) return TPMLP_ERR_HIP;
+    s->D = D;
+    s->F = F;
+    s->n = n;
+    s->dtype = dtype;
+    s->packed = packed;
+    s->packed_bytes = packed_bytes;
+    s->ws = nullptr;
+    s->ws_bytes = 0;
+
+    // Pair i of "The split" is rows iF/n..(i+1)F/n-1 of A^T and columns
+    // iF/n..(i+1)F/n-1 of B^T: one transpose of each matrix packs all pairs,
+    // each K-contiguous for the matrix cores.
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int eb = (int)elem_size(dtype);
+    char* at = static_cast<char*>(packed);
+    char* bt = at + round_up((size_t)D * (size_t)F * eb);
+    hipError_t e = launch_transpose(A, F, at, D, D, F, eb, hs);        // A (D x F) -> A^T (F x D)
+    if (e == hipSuccess) e = launch_transpose(B, D, bt, F, F, D, eb, hs);  // B (F x D) -> B^T (D x F)
+    if (e != hipSuccess) {
+        delete s;
+        return TPMLP_ERR_HIP;
+    }
+    *out = s;
+    return TPMLP_OK;
+}
+
+int tpmlp_shard_count(const tpmlp_shards* s) { return s ? s->n : 0; }
+
+tpmlp_status tpmlp_shard_info(const tpmlp_shards* s, int64_t* D, int64_t* F, int* n, int* dtype) {
+    if (!s) return TPMLP_ERR_NULL;
+    if (D) *D = s->D;
+    if (F) *F = s->F;
+    if (n) *n = s->n;
+    if (dtype) *dtype = s->dtype;
+    return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_shard_unpack(const tpmlp_shards* s, int i, void* A_i, void* B_i, void* stream) {
+    if (!s) return TPMLP_ERR_NULL;
+    if (i < 0 || i >= s->n) return TPMLP_ERR_SHAPE;
+    if ((A_i && !aligned16(A_i)) || (B_i && !aligned16(B_i))) return TPMLP_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int eb = (int)elem_size(s->dtype);
+    const int64_t w = s->F / s->n;
+    const char* at = static_cast<const char*>(s->packed);
+    const char* bt = at + round_up((size_t)s->D * (size_t)s->F * eb);
+    hipError_t e = hipSuccess;
+    if (A_i)  // rows i*w.. of A^T (w x D) -> A_i (D x w)
+        e = launch_transpose(at + (size_t)i * w * s->D * eb, s->D, A_i, w, w, s->D, eb, hs);
+    if (e == hipSuccess && B_i)  // columns i*w.. of B^T (D x w, pitch F) -> B_i (w x D)
+        e = launch_transpose(bt + (size_t)i * w * eb, s->F, B_i, s->D, s->D, w, eb, hs);
+    return from_hip(e);
+}
+
+void tpmlp_shards_destroy(tpmlp_shards* s) { delete s; }
+
+size_t tpmlp_forward_workspace_bytes(const tpmlp_shards* s, int64_t M, int flags, int single_shard) {
+    if (!s || M < 0 || M > kMaxDim) return 0;
+    return ws_layout(s, M, flags, single_shard).total;
+}
+
+tpmlp_status tpmlp_set_workspace(tpmlp_shards* s, void* ws, size_t bytes) {
+    if (!s) return TPMLP_ERR_NULL;
+    if (ws && !aligned16(ws)) return TPMLP_ERR_ALIGN;
+    s->ws = ws;
+    s->ws_bytes = ws ? bytes : 0;
+    return TPMLP_OK;
+}
+
+void tpmlp_opts_init(tpmlp_opts* o) {
+    if (!o) return;
+    std::memset(o, 0, sizeof(*o));
+    o->ln_eps = 1e-5f;
+    o->y_dtype = -1;
+    o->shard_index = -1;
+}
+
+tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, void* Y,
+                              const tpmlp_opts* opts, void* stream) {
+    tpmlp_opts o;
+    tpmlp_opts_init(&o);
+    if (opts) o = *opts;
+    if (!s) return TPMLP_ERR_NULL;
+    if (M < 0 || M > kMaxDim) return TPMLP_ERR_SHAPE;
+    if (o.flags & ~TPMLP_OPT_LAYERNORM) return TPMLP_ERR_SHAPE;
+    const int y_dtype = o.y_dtype < 0 ? s->dtype : o.y_dtype;
+    if (!valid_dtype(y_dtype)) return TPMLP_ERR_DTYPE;
+    if (s->dtype == TPMLP_F32 && y_dtype != TPMLP_F32) return TPMLP_ERR_DTYPE;
+    if (o.shard_index < -1 || o.shard_index >= s->n) return TPMLP_ERR_SHAPE;
+    const bool ln = (o.flags & TPMLP_OPT_LAYERNORM) != 0;
+    const float eps = o.ln_eps > 0.f ? o.ln_eps : 1e-5f;
+    if (!(eps < 1e30f)) return TPMLP_ERR_SHAPE;
+    if (M == 0) return TPMLP_OK;
+    if (!X || !Y) return TPMLP_ERR_NULL;
+    if (!aligned16(X) || !aligned16(Y) || (o.residual && !aligned16(o.residual))) return TPMLP_ERR_ALIGN;
+
+    const bool single = o.shard_index >= 0;
+    void* ws = o.workspace ? o.workspace : s->ws;
+    const size_t ws_bytes = o.workspace ? o.workspace_bytes : s->ws_bytes;
+    const WsLayout L = ws_layout(s, M, o.flags, single);
+    if (!ws || ws_bytes < L.total) return TPMLP_ERR_WORKSPACE;
+    if (!aligned16(ws)) return TPMLP_ERR_ALIGN;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (o.events)
+        for (int k = 0; k < 4; ++k) ev[k] = static_cast<hipEvent_t>(o.events[k]);
+    auto mark = [&](int k) -> hipError_t { return ev[k] ? hipEventRecord(ev[k], hs) : hipSuccess; };
+
+    const int64_t D = s->D, F = s->F, w = F / s->n;
+    const int64_t n_lo = single ? o.shard_index * w : 0;
+    const int64_t nh = single ? w : F;
+    const int eb = (int)elem_size(s->dtype);
+    const char* at = static_cast<const char*>(s->packed);
+    const char* bt = at + round_up((size_t)D * (size_t)F * eb);
+    char* wsb = static_cast<char*>(ws);
+    void* H = wsb + L.h_off;
+    float* mean = ln ? reinterpret_cast<float*>(wsb + L.mean_off) : nullptr;
+    float* rstd = ln ? reinterpret_cast<float*>(wsb + L.rstd_off) : nullptr;
+
+    hipError_t e = mark(0);
+    if (e == hipSuccess && ln) e = launch_ln_stats(X, M, D, s->dtype, eps, mean, rstd, hs);
+    if (e == hipSuccess) e = mark(1);
+
+    // GEMM1, column-parallel: H[:, 0:nh] = GeLU(LN?(X) . A^T[n_lo:n_lo+nh, :]^T)
+    if (e == hipSuccess) {
+        GemmArgs g1;
+        g1.A = X; g1.lda = D;
+        g1.B = at + (size_t)n_lo * D * eb; g1.ldb = D;
+        g1.M = M; g1.N = nh; g1.K = D;
+        g1.C = H; g1.ldc = nh; g1.c_dtype = s->dtype;
+        g1.ln_mean = mean; g1.ln_rstd = rstd;
+        g1.epi = kEpiGelu;
+        g1.ab_dtype = s->dtype;
+        e = launch_gemm(g1, hs);
+    }
+    if (e == hipSuccess) e = mark(2);
+
+    // GEMM2, row-parallel with the shard sum in the accumulator:
+    // Y = H[:, 0:nh] . B^T[:, n_lo:n_lo+nh]^T (+ residual)
+    if (e == hipSuccess) {
+        GemmArgs g2;
+        g2.A = H; g2.lda = nh;
+        g2.B = bt + (size_t)n_lo * eb; g2.ldb = F;
+        g2.M = M; g2.N = D; g2.K = nh;
+        g2.C = Y; g2.ldc = D; g2.c_dtype = y_dtype;
+        g2.R = o.residual; g2.ldr = D;
+        g2.epi = kEpiStore;
+        g2.ab_dtype = s->dtype;
+        e = launch_gemm(g2, hs);
+    }
+    if (e == hipSuccess) e = mark(3);
+    return from_hip(e);
+}
+
+tpmlp_status tpmlp_forward(const void* X, int64_t M, const tpmlp_shards* s, void* Y, void* stream) {
+    return tpmlp_forward_ex(X, M, s, Y, nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,239 @@
+"""Python binding of libtpmlp.so (argument marshalling only).
+
+The names follow "Tensor-Parallel MLP (Megatron)", section "What to
+implement": ``gelu(x)``, ``shard_mlp(A, B, n)`` and ``tp_mlp(X, shards)``.
+Every step of the computation runs in the HIP kernels behind the C ABI
+(include/tpmlp.h); this module only allocates outputs and workspaces with
+torch on the tensors' device and passes raw device pointers and the current
+stream.  There is no fallback: if the library is not built, or a tensor is
+not on a GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libtpmlp.so")
+
+F32, BF16 = 0, 1
+OPT_LAYERNORM = 1
+STATUS_NAMES = {
+    0: "TPMLP_OK", 1: "TPMLP_ERR_NULL", 2: "TPMLP_ERR_SHAPE", 3: "TPMLP_ERR_INDIVISIBLE",
+    4: "TPMLP_ERR_DTYPE", 5: "TPMLP_ERR_WORKSPACE", 6: "TPMLP_ERR_ALIGN", 7: "TPMLP_ERR_HIP",
+}
+
+# every function declared in include/tpmlp.h, with its ctypes signature
+_c_i64, _c_int, _c_vp, _c_sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+
+
+class Opts(ctypes.Structure):
+    """Mirror of tpmlp_opts."""
+    _fields_ = [("flags", ctypes.c_int), ("ln_eps", ctypes.c_float), ("y_dtype", ctypes.c_int),
+                ("residual", ctypes.c_void_p), ("shard_index", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("events", ctypes.c_void_p)]
+
+
+SIGNATURES = {
+    "tpmlp_status_string": (ctypes.c_char_p, [_c_int]),
+    "tpmlp_version": (ctypes.c_char_p, []),
+    "tpmlp_gelu": (_c_int, [_c_vp, _c_vp, _c_i64, _c_int, _c_vp]),
+    "tpmlp_shard_bytes": (_c_sz, [_c_i64, _c_i64, _c_int, _c_int]),
+    "tpmlp_shard": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_sz,
+                             ctypes.POINTER(_c_vp), _c_vp]),
+    "tpmlp_shard_count": (_c_int, [_c_vp]),
+    "tpmlp_shard_info": (_c_int, [_c_vp, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64),
+                                  ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+    "tpmlp_shard_unpack": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_vp]),
+    "tpmlp_shards_destroy": (None, [_c_vp]),
+    "tpmlp_forward_workspace_bytes": (_c_sz, [_c_vp, _c_i64, _c_int, _c_int]),
+    "tpmlp_set_workspace": (_c_int, [_c_vp, _c_vp, _c_sz]),
+    "tpmlp_forward": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "tpmlp_opts_init": (None, [ctypes.POINTER(Opts)]),
+    "tpmlp_forward_ex": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, ctypes.POINTER(Opts), _c_vp]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m tensor_transformer_mlp_tpmlp_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class TpmlpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().tpmlp_status_string(status).decode()
+        super().__init__(f"{where}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise TpmlpError(status, where)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.float32 if code == F32 else torch.bfloat16
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def gelu(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Elementwise tanh-GeLU on the GPU (tpmlp_gelu)."""
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.numel() != x.numel():
+        raise ValueError("out must match x in dtype and size")
+    _check(lib().tpmlp_gelu(_dev(x, "x"), _dev(out, "out"), x.numel(), _dtype_code(x.dtype),
+                            _stream(x.device)), "tpmlp_gelu")
+    return out
+
+
+class Shards:
+    """n (A_i, B_i) pairs packed on the GPU (a tpmlp_shards descriptor).
+
+    Holds the packed weight buffer (owned here, as a torch tensor) and a
+    grow-only forward workspace.
+    """
+
+    def __init__(self, handle: int, packed: torch.Tensor, D: int, F: int, n: int, dtype: torch.dtype):
+        self._handle = handle
+        self.packed = packed
+        self.D, self.F, self.n, self.dtype = D, F, n, dtype
+        self.device = packed.device
+        self._ws: Optional[torch.Tensor] = None
+
+    @property
+    def handle(self) -> int:
+        return self._handle
+
+    def __len__(self) -> int:
+        return self.n
+
+    def pairs(self) -> List[Tuple[torch.Tensor, torch.Tensor]]:
+        """Unpack every pair to the page's layout: A_i (D x F/n), B_i (F/n x D)."""
+        w = self.F // self.n
+        out = []
+        for i in range(self.n):
+            A_i = torch.empty((self.D, w), dtype=self.dtype, device=self.device)
+            B_i = torch.empty((w, self.D), dtype=self.dtype, device=self.device)
+            _check(lib().tpmlp_shard_unpack(self._handle, i, A_i.data_ptr(), B_i.data_ptr(),
+                                            _stream(self.device)), "tpmlp_shard_unpack")
+            out.append((A_i, B_i))
+        return out
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def close(self) -> None:
+        if self._handle:
+            lib().tpmlp_shards_destroy(self._handle)
+            self._handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def shard_mlp(A: torch.Tensor, B: torch.Tensor, n: int) -> Shards:
+    """Split A (D x F) by columns and B (F x D) by rows into n pairs (tpmlp_shard)."""
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be matrices")
+    D, F = A.shape
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same dtype")
+    if B.shape != (F, D):
+        raise ValueError(f"B must be ({F}, {D}), got {tuple(B.shape)}")
+    dt = _dtype_code(A.dtype)
+    L = lib()
+    nbytes = L.tpmlp_shard_bytes(D, F, n, dt)
+    packed = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=A.device)
+    h = ctypes.c_void_p()
+    _check(L.tpmlp_shard(_dev(A, "A"), _dev(B, "B"), D, F, n, dt, packed.data_ptr(), packed.numel(),
+                         ctypes.byref(h), _stream(A.device)), "tpmlp_shard")
+    return Shards(h.value, packed, D, F, n, A.dtype)
+
+
+def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, eps: float = 1e-5,
+           residual: Optional[torch.Tensor] = None, shard_index: int = -1,
+           out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+           events: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """Y = sum_i GeLU(X A_i) B_i on the GPU (tpmlp_forward_ex).
+
+    layernorm: normalise each row of X first (no affine); residual: added once
+    after the shard sum; shard_index: return only partial Y_i; events: four
+    hipEvent_t handles recorded around the kernels (timing hook).
+    """
+    if X.dim() != 2 or X.shape[1] != shards.D:
+        raise ValueError(f"X must be (M, {shards.D})")
+    if X.dtype != shards.dtype:
+        raise TypeError("X must have the weights' dtype")
+    M = X.shape[0]
+    y_dtype = shards.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, shards.D), dtype=y_dtype, device=X.device)
+    elif out.dtype != y_dtype or tuple(out.shape) != (M, shards.D):
+        raise ValueError("out has the wrong dtype or shape")
+    flags = OPT_LAYERNORM if layernorm else 0
+    L = lib()
+    nbytes = L.tpmlp_forward_workspace_bytes(shards.handle, M, flags, 1 if shard_index >= 0 else 0)
+    ws = shards.workspace(nbytes)
+    o = Opts()
+    L.tpmlp_opts_init(ctypes.byref(o))
+    o.flags = flags
+    o.ln_eps = eps
+    o.y_dtype = _dtype_code(y_dtype)
+    if residual is not None:
+        if residual.dtype != X.dtype or tuple(residual.shape) != (M, shards.D):
+            raise ValueError("residual must match X")
+        o.residual = _dev(residual, "residual")
+    o.shard_index = shard_index
+    o.workspace = ws.data_ptr()
+    o.workspace_bytes = ws.numel()
+    ev_arr = None
+    if events is not None:
+        ev_arr = (ctypes.c_void_p * 4)(*[e or None for e in events])
+        o.events = ctypes.cast(ev_arr, ctypes.c_void_p)
+    _check(L.tpmlp_forward_ex(_dev(X, "X") if M else X.data_ptr(), M, shards.handle,
+                              _dev(out, "out") if M else out.data_ptr(), ctypes.byref(o),
+                              _stream(X.device)), "tpmlp_forward_ex")
+    return out
