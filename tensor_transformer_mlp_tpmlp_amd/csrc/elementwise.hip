@@ -95,6 +95,34 @@ hipError_t launch_ln_stats(const void* x, int64_t M, int64_t D, int dtype, float
 }
 
 // ---------------------------------------------------------------------------
+// Row sums in fp32, one wave per row: the column sums of A (row sums of the
+// packed A^T) that the LayerNorm epilogue of the first GEMM needs.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void rowsum_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                     float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const T* xr = x + row * cols;
+    float s = 0.f;
+    for (int64_t c = lane; c < cols; c += 64) s += to_f32(xr[c]);
+    s = wave_sum(s);
+    if (lane == 0) out[row] = s;
+}
+
+hipError_t launch_rowsum(const void* x, int64_t rows, int64_t cols, int dtype, float* out, hipStream_t stream) {
+    const int64_t blocks = (rows + 3) / 4;
+    if (dtype == kF32)
+        rowsum_kernel<float><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+            static_cast<const float*>(x), rows, cols, out);
+    else
+        rowsum_kernel<bf16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+            static_cast<const bf16*>(x), rows, cols, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Strided transpose out[c][r] = in[r][c] (r < R, c < C), bit-exact, through a
 // 64x64 LDS tile padded by one element against bank conflicts.  Used to pack
 // A (D x F) into K-contiguous A^T (F x D) and B (F x D) into B^T (D x F), and

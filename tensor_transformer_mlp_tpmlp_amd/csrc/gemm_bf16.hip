@@ -1,6 +1,6 @@
 // Throughput GEMM for bf16 operands on gfx950 matrix cores.
 //
-// C[m][n] = epi( sum_k a(m,k) * Bop[n][k] ), Aop (M x K) and Bop (N x K)
+// C[m][n] = epi( sum_k Aop[m][k] * Bop[n][k] ), Aop (M x K) and Bop (N x K)
 // K-contiguous, fp32 accumulation in v_mfma_f32_32x32x16_bf16.
 //
 // Both GEMMs of the TP-MLP run here:
@@ -13,15 +13,31 @@
 //     partials Y_i are summed in the same fp32 accumulator and never leave
 //     the chip.
 //
-// Tiling: one 256x256 output tile per workgroup of 4 waves (2x2), each wave
-// owning a 128x128 sub-tile (4x4 MFMA 32x32 blocks, 256 fp32 accumulators per
-// lane).  K advances in steps of 64 through a double-buffered LDS ring
-// (2 stages x (32 KiB A + 32 KiB B) = 128 KiB of the 160 KiB LDS), with the
-// next step's global loads in flight while the matrix cores work on the
-// current one.  LDS rows are 128 bytes (64 bf16) with the 16-byte chunks
-// XOR-swizzled so both the row-wise stores and the 32-row MFMA operand reads
-// are bank-conflict free.  Workgroups are mapped so that each XCD works on a
-// contiguous band of output tiles, grouped 8 tile-rows at a time for L2 reuse.
+// Tiling: one 256x256 output tile per workgroup of 4 waves (2x2, one wave per
+// SIMD), each wave owning a 128x128 sub-tile: 4x4 MFMA 32x32 blocks, 256 fp32
+// accumulators per lane held in AGPRs.  K advances in steps of 64 through two
+// LDS stages of 64 KiB (A tile 32 KiB + B tile 32 KiB).
+//
+// Global -> LDS moves use the direct-to-LDS buffer load (buffer_load_dwordx4
+// ... lds): no VGPR staging and no ds_write.  Lane L of a wave's load lands at
+// LDS base + 16 L, so the XOR swizzle of the LDS layout is applied on the
+// global side by choosing which 16-byte chunk each lane fetches.
+//
+// Pipeline per K step of tile t (k-sub-steps kk = 0..3, 16 MFMAs each):
+//   kk = 0..2: read the MFMA fragments of kk+1 from LDS while the matrix
+//              cores run kk;
+//   kk = 3   : wait until this wave's LDS reads and tile t+1's loads have
+//              landed, barrier (tile t+1 visible to all waves, tile t's stage
+//              free), issue tile t+2's loads into the freed stage, read tile
+//              t+1's first fragments, then run kk = 3.
+// So global loads have a whole K step (2048 MFMA cycles) to arrive, LDS reads
+// are always one sub-step ahead, and there is one barrier per K step.
+//
+// LayerNorm prologue (FFN half of the Post-LN block, "LLM Lab Notes 06",
+// section 2, marker 5) is applied algebraically in GEMM1's epilogue:
+//   sum_k (x_k - mu) r a_k = r * (sum_k x_k a_k - mu * sum_k a_k),
+// with the per-row mean mu and r = 1/sqrt(var + eps) from the statistics
+// kernel and the per-column sums of A from shard time.
 #include "device_common.h"
 #include "launch.h"
 
@@ -32,7 +48,8 @@ namespace {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int TILE_BYTES = BM * BK * 2;  // one operand, one stage
+constexpr int TILE_BYTES = BM * BK * 2;     // one operand tile of one stage: 32 KiB
+constexpr int LOADS_PER_TILE = 16;          // direct loads per wave per K step (8 A + 8 B)
 
 struct FastParams {
     const bf16* A;
@@ -44,19 +61,23 @@ struct FastParams {
     int64_t ldc;
     const bf16* R;
     int64_t ldr;
-    const float* mean;
+    const float* mean;   // LayerNorm: per-row mean and 1/sqrt(var+eps)
     const float* rstd;
+    const float* csum;   // LayerNorm: per-column sums of Bop (= column sums of A)
     int tiles_m, tiles_n;
 };
 
+// s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]; a field at its maximum does not wait.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
+
 // Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row` in LDS.  The
-// XOR key (row & 7) ^ ((row >> 3) & 1) makes any 8 consecutive rows, and the
-// even and the odd rows of any 16 consecutive rows, land on distinct chunks,
-// which keeps 128-bit accesses conflict-free whether the LDS serves 8 or 16
-// lanes per cycle.
-__device__ __forceinline__ uint32_t swz(int row, int chunk) {
-    return (uint32_t)(row * 128 + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 4));
-}
+// XOR key (row & 7) ^ ((row >> 3) & 1) puts any 8 consecutive rows, and the
+// even and the odd rows of any 16 consecutive rows, on distinct chunks, which
+// keeps 128-bit accesses conflict-free whether the LDS serves 8 or 16 lanes
+// per cycle.
+__device__ __forceinline__ uint32_t lds_key(int row) { return (uint32_t)((row & 7) ^ ((row >> 3) & 1)); }
 
 // Blocks reach the 8 XCDs round-robin (block b runs on XCD b % 8).  Give each
 // XCD a contiguous range of tile ids, and walk that range in groups of 8 tile
@@ -77,75 +98,72 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
     tn = local / gm;
 }
 
-template <int EPI, bool LN, typename TC>
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int EPI, bool LN, bool ODD, typename TC>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TILE_BYTES];
+    // two pipeline stages as distinct objects so the compiler can tell the
+    // stage being filled from the stage being read
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[2 * TILE_BYTES];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int w = t >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, kept in an SGPR
     const int wm = w >> 1, wn = w & 1;
     int tm, tn;
     map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
 
-    // Global -> LDS staging: thread t moves 16-byte chunk (t & 7) of rows
-    // (t >> 3) + 32 j, j < 8, of both operand tiles.
-    const int lrow = t >> 3, lch = t & 7;
-    const char* a_base = reinterpret_cast<const char*>(p.A + m0 * p.lda);
-    const char* b_base = reinterpret_cast<const char*>(p.B + n0 * p.ldb);
-    const uint32_t a_off = (uint32_t)(lrow * p.lda * 2 + lch * 16);
-    const uint32_t b_off = (uint32_t)(lrow * p.ldb * 2 + lch * 16);
-    const uint32_t a_step = (uint32_t)(32 * p.lda * 2);
-    const uint32_t b_step = (uint32_t)(32 * p.ldb * 2);
-    const uint32_t st_off = swz(lrow, lch);  // + j * 32 rows * 128 bytes
+    // Buffer resources over this tile's 256 rows of each operand.
+    const uint32_t a_bytes = (uint32_t)(BM * p.lda * 2);
+    const uint32_t b_bytes = (uint32_t)(BN * p.ldb * 2);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>(p.A + m0 * p.lda), (short)0, (int)a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>(p.B + n0 * p.ldb), (short)0, (int)b_bytes, 0x00020000);
 
-    float ln_mu[8], ln_rs[8];
-    if constexpr (LN) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ln_mu[j] = p.mean[m0 + lrow + 32 * j];
-            ln_rs[j] = p.rstd[m0 + lrow + 32 * j];
-        }
-    }
+    // Wave w fills tile rows [64 w, 64 w + 64) of each operand with 8 loads of
+    // 8 rows; in load q, lane L fills row 64 w + 8 q + L/8 at physical chunk
+    // L % 8, which must hold logical chunk (L % 8) ^ key(row), and
+    // key(row) = (L / 8) ^ (q & 1).
+    const uint32_t lrow = (uint32_t)(w * 64 + (lane >> 3));
+    const uint32_t cx0 = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+    const uint32_t cx1 = cx0 ^ 16u;
+    const uint32_t a_v0 = lrow * (uint32_t)(p.lda * 2) + cx0, a_v1 = a_v0 - cx0 + cx1;
+    const uint32_t b_v0 = lrow * (uint32_t)(p.ldb * 2) + cx0, b_v1 = b_v0 - cx0 + cx1;
+    const uint32_t a_qstep = (uint32_t)(8 * p.lda * 2);
+    const uint32_t b_qstep = (uint32_t)(8 * p.ldb * 2);
+    const uint32_t dst_w = (uint32_t)(w * 64 * 128);
 
-    u32x4 ra[8], rb[8];
-    auto gload = [&](int k0) {
-        const char* ab = a_base + (int64_t)k0 * 2;
-        const char* bb = b_base + (int64_t)k0 * 2;
+    auto load_tile = [&](uint8_t* st, int k0) {
+        const uint32_t kb = (uint32_t)k0 * 2u;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ra[j] = *reinterpret_cast<const u32x4*>(ab + a_off + j * a_step);
-            rb[j] = *reinterpret_cast<const u32x4*>(bb + b_off + j * b_step);
-        }
-    };
-    auto lstore = [&](int stage) {
-        uint8_t* as = smem + stage * 2 * TILE_BYTES;
-        uint8_t* bs = as + TILE_BYTES;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            u32x4 v = ra[j];
-            if constexpr (LN) {
-                bf16 e[8];
-                __builtin_memcpy(e, &v, 16);
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    e[q] = static_cast<bf16>((static_cast<float>(e[q]) - ln_mu[j]) * ln_rs[j]);
-                __builtin_memcpy(&v, e, 16);
-            }
-            *reinterpret_cast<u32x4*>(as + st_off + j * 4096) = v;
-            *reinterpret_cast<u32x4*>(bs + st_off + j * 4096) = rb[j];
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + dst_w + q * 1024),
+                                                     16, (q & 1) ? a_v1 : a_v0, kb + q * a_qstep, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + TILE_BYTES + dst_w + q * 1024),
+                                                     16, (q & 1) ? b_v1 : b_v0, kb + q * b_qstep, 0, 0);
         }
     };
 
     // MFMA operand reads: lane l reads row (l & 31) of each 32-row block at
-    // chunk 2*kk + (l >> 5); the swizzle key of those rows depends on the
-    // lane only.
-    const int key = (lane & 7) ^ ((lane >> 3) & 1);
+    // logical chunk 2 kk + (l >> 5); the swizzle key of those rows depends on
+    // the lane only.
+    const uint32_t key = lds_key(lane & 31);
     const int hi = lane >> 5;
     const uint32_t a_rd = (uint32_t)((wm * 128 + (lane & 31)) * 128);
     const uint32_t b_rd = (uint32_t)((wn * 128 + (lane & 31)) * 128) + TILE_BYTES;
+
+    auto read_frags = [&](const uint8_t* st, int kk, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+        const uint32_t ch = (((uint32_t)(2 * kk + hi)) ^ key) << 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            fa[i] = *reinterpret_cast<const bf16x8*>(st + a_rd + i * 32 * 128 + ch);
+            fb[i] = *reinterpret_cast<const bf16x8*>(st + b_rd + i * 32 * 128 + ch);
+        }
+    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -153,31 +171,95 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+    auto mfma16 = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
     const int nk = p.K / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-        const uint8_t* st = smem + cur * 2 * TILE_BYTES;
+    __builtin_assume(nk >= 2);
+
+    // Instruction order inside a K step is pinned with scheduling groups
+    // (mask 0x008 = MFMA, 0x100 = LDS read, 0x020 = VMEM read): the LDS reads
+    // of the next sub-step, and the next tile's global loads, are interleaved
+    // one by one with the current sub-step's MFMAs.
+    auto interleave_reads = [&]() {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const uint32_t ch = (uint32_t)(((2 * kk + hi) ^ key) << 4);
-            bf16x8 a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = *reinterpret_cast<const bf16x8*>(st + a_rd + i * 32 * 128 + ch);
-                b[i] = *reinterpret_cast<const bf16x8*>(st + b_rd + i * 32 * 128 + ch);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        if (kt + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One K step on the tile held in `cur`.  has_next: a next tile exists (in
+    // `nxt`); do_load: also refill `cur` with the tile two steps ahead.
+    auto k_step = [&](uint8_t* cur, uint8_t* nxt, int k_load, bool has_next, bool do_load) {
+        read_frags(cur, 1, fa1, fb1);
+        mfma16(fa0, fb0);
+        interleave_reads();
+        read_frags(cur, 2, fa0, fb0);
+        mfma16(fa1, fb1);
+        interleave_reads();
+        read_frags(cur, 3, fa1, fb1);
+        mfma16(fa0, fb0);
+        interleave_reads();
+        if (has_next) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (do_load) load_tile(cur, k_load);
+            read_frags(nxt, 0, fa0, fb0);
+            mfma16(fa1, fb1);
+            if (do_load) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                interleave_reads();
+            }
+        } else {
+            mfma16(fa1, fb1);
+        }
+    };
+
+    load_tile(stage0, 0);
+    if (nk > 1) {
+        load_tile(stage1, BK);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_TILE));
+    } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    read_frags(stage0, 0, fa0, fb0);
+
+    // Steady state, branch-free: tiles kt (stage 0) and kt+1 (stage 1), each
+    // refilling its stage with the tile two ahead.
+    int kt = 0;
+    for (; kt + 3 < nk; kt += 2) {
+        k_step(stage0, stage1, (kt + 2) * BK, true, true);
+        k_step(stage1, stage0, (kt + 3) * BK, true, true);
+    }
+    // The last two (even step count) or three (odd) tiles, as straight-line
+    // code: one tail shape per instantiation keeps the accumulators in AGPRs.
+    if constexpr (ODD) {
+        k_step(stage0, stage1, (kt + 2) * BK, true, true);
+        k_step(stage1, stage0, 0, true, false);
+        k_step(stage0, stage1, 0, false, false);
+    } else {
+        k_step(stage0, stage1, 0, true, false);
+        k_step(stage1, stage0, 0, false, false);
     }
 
     // Epilogue.  Accumulator layout of a 32x32 MFMA: lane l holds column
@@ -185,13 +267,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
     TC* __restrict__ C = static_cast<TC*>(p.C);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        const int64_t mb = m0 + wm * 128 + i * 32 + hi * 4;
+        float rs[16], rm[16];
+        if constexpr (LN) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = mb + (r >> 2) * 8 + (r & 3);
+                rs[r] = p.rstd[m];
+                rm[r] = rs[r] * p.mean[m];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+            float cs = 0.f;
+            if constexpr (LN) cs = p.csum[n];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+                const int64_t m = mb + (r >> 2) * 8 + (r & 3);
                 float v = acc[i][j][r];
+                if constexpr (LN) v = __builtin_fmaf(rs[r], v, -rm[r] * cs);
                 if constexpr (EPI == kEpiGelu) {
                     v = gelu_tanh(v);
                 } else {
@@ -211,14 +306,18 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
     p.M = (int)g.M; p.N = (int)g.N; p.K = (int)g.K;
     p.C = g.C; p.ldc = g.ldc;
     p.R = static_cast<const bf16*>(g.R); p.ldr = g.ldr;
-    p.mean = g.ln_mean; p.rstd = g.ln_rstd;
+    p.mean = g.ln_mean; p.rstd = g.ln_rstd; p.csum = g.ln_csum;
     p.tiles_m = (int)(g.M / BM);
     p.tiles_n = (int)(g.N / BN);
     const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n);
-    if (g.ln_mean)
-        gemm_bf16_256x256<EPI, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-    else
-        gemm_bf16_256x256<EPI, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+    const bool odd = (g.K / BK) & 1;
+    if (g.ln_mean) {
+        if (odd) gemm_bf16_256x256<EPI, true, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+        else gemm_bf16_256x256<EPI, true, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+    } else {
+        if (odd) gemm_bf16_256x256<EPI, false, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+        else gemm_bf16_256x256<EPI, false, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+    }
     return hipGetLastError();
 }
 
@@ -227,18 +326,20 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // The 256x256 kernel takes bf16 operands whose M and N are whole tiles, K a
-// whole number of 64-wide steps, 16-byte aligned rows, and byte offsets of
-// one 256-row operand tile that fit in 32 bits.
+// whole number (at least two) of 64-wide steps, 16-byte aligned rows, byte offsets of one
+// 256-row operand tile below 2^31 (buffer offsets), and, with the LayerNorm
+// epilogue, the column sums of Bop.
 GemmPath choose_gemm_path(const GemmArgs& g) {
     if (g.ab_dtype != kBF16) return kPathGeneric;
     if (g.M <= 0 || g.N <= 0 || g.K <= 0) return kPathGeneric;
-    if (g.M % BM || g.N % BN || g.K % BK) return kPathGeneric;
+    if (g.M % BM || g.N % BN || g.K % BK || g.K < 2 * BK) return kPathGeneric;
     if (g.lda % 8 || g.ldb % 8 || !aligned16(g.A) || !aligned16(g.B)) return kPathGeneric;
-    if ((int64_t)BM * g.lda * 2 >= (int64_t)1 << 32 || (int64_t)BN * g.ldb * 2 >= (int64_t)1 << 32)
+    if ((int64_t)BM * g.lda * 2 >= ((int64_t)1 << 31) || (int64_t)BN * g.ldb * 2 >= ((int64_t)1 << 31))
         return kPathGeneric;
     if ((g.M / BM) * (g.N / BN) >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) ||
         g.N >= ((int64_t)1 << 31) || g.K >= ((int64_t)1 << 31))
         return kPathGeneric;
+    if (g.ln_mean && !g.ln_csum) return kPathGeneric;
     return kPathFastBf16;
 }
 

@@ -17,7 +17,7 @@ struct tpmlp_shards {
     int64_t F;
     int n;
     int dtype;
-    void* packed;        // A^T (F x D) followed by B^T (D x F), both `dtype`
+    void* packed;        // A^T (F x D), B^T (D x F), both `dtype`, then F fp32 column sums of A
     size_t packed_bytes;
     void* ws;            // bound workspace (caller-owned)
     size_t ws_bytes;
@@ -99,7 +99,7 @@ tpmlp_status tpmlp_gelu(const void* x, void* y, int64_t count, int dtype, void* 
 
 size_t tpmlp_shard_bytes(int64_t D, int64_t F, int n, int dtype) {
     if (check_shard_args(D, F, n, dtype) != TPMLP_OK) return 0;
-    return round_up((size_t)D * (size_t)F * elem_size(dtype)) * 2;
+    return round_up((size_t)D * (size_t)F * elem_size(dtype)) * 2 + round_up((size_t)F * 4);
 }
 
 tpmlp_status tpmlp_shard(const void* A, const void* B, int64_t D, int64_t F, int n, int dtype,
@@ -129,8 +129,10 @@ tpmlp_status tpmlp_shard(const void* A, const void* B, int64_t D, int64_t F, int
     const int eb = (int)elem_size(dtype);
     char* at = static_cast<char*>(packed);
     char* bt = at + round_up((size_t)D * (size_t)F * eb);
+    float* csum = reinterpret_cast<float*>(bt + round_up((size_t)D * (size_t)F * eb));
     hipError_t e = launch_transpose(A, F, at, D, D, F, eb, hs);        // A (D x F) -> A^T (F x D)
     if (e == hipSuccess) e = launch_transpose(B, D, bt, F, F, D, eb, hs);  // B (F x D) -> B^T (D x F)
+    if (e == hipSuccess) e = launch_rowsum(at, F, D, dtype, csum, hs);  // column sums of A
     if (e != hipSuccess) {
         delete s;
         return TPMLP_ERR_HIP;
@@ -228,6 +230,7 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
     const int eb = (int)elem_size(s->dtype);
     const char* at = static_cast<const char*>(s->packed);
     const char* bt = at + round_up((size_t)D * (size_t)F * eb);
+    const float* csum = reinterpret_cast<const float*>(bt + round_up((size_t)D * (size_t)F * eb));
     char* wsb = static_cast<char*>(ws);
     void* H = wsb + L.h_off;
     float* mean = ln ? reinterpret_cast<float*>(wsb + L.mean_off) : nullptr;
@@ -245,6 +248,7 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
         g1.M = M; g1.N = nh; g1.K = D;
         g1.C = H; g1.ldc = nh; g1.c_dtype = s->dtype;
         g1.ln_mean = mean; g1.ln_rstd = rstd;
+        g1.ln_csum = ln ? csum + n_lo : nullptr;
         g1.epi = kEpiGelu;
         g1.ab_dtype = s->dtype;
         e = launch_gemm(g1, hs);
