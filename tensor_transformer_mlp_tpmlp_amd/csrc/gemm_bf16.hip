@@ -15,7 +15,9 @@
 //
 // Tiling: one 256x256 output tile per workgroup of 4 waves (2x2, one wave per
 // SIMD), each wave owning a 128x128 sub-tile: 4x4 MFMA 32x32 blocks, 256 fp32
-// accumulators per lane held in AGPRs.  K advances in steps of 64 through two
+// accumulators per lane held in AGPRs.  Shapes too small to fill the GPU with
+// 256x256 tiles use 128x128 tiles (2x2 blocks per wave, 64 KiB of LDS, two
+// workgroups per CU) with the same pipeline.  K advances in steps of 64 through two
 // LDS stages of 64 KiB (A tile 32 KiB + B tile 32 KiB).
 //
 // Global -> LDS moves use the direct-to-LDS buffer load (buffer_load_dwordx4
@@ -45,11 +47,16 @@ namespace tpmlp {
 
 namespace {
 
-constexpr int BM = 256;
-constexpr int BN = 256;
+// WB = MFMA blocks of 32x32 per wave per side: 4 gives the 256x256 tile
+// (128x128 per wave), 2 the 128x128 tile (64x64 per wave) used when 256x256
+// tiles would leave CUs idle.
 constexpr int BK = 64;
-constexpr int TILE_BYTES = BM * BK * 2;     // one operand tile of one stage: 32 KiB
-constexpr int LOADS_PER_TILE = 16;          // direct loads per wave per K step (8 A + 8 B)
+template <int WB> struct Tile {
+    static constexpr int M = 64 * WB;         // tile rows (= tile columns)
+    static constexpr int BYTES = M * BK * 2;  // one operand tile of one stage
+    static constexpr int QLOADS = M / 32;     // direct loads per wave per operand per K step
+    static constexpr int LOADS = 2 * QLOADS;  // per wave per K step
+};
 
 struct FastParams {
     const bf16* A;
@@ -100,8 +107,11 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int EPI, bool LN, bool ODD, typename TC>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
+template <int WB, int EPI, bool LN, bool ODD, typename TC>
+__global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
+    constexpr int BM = Tile<WB>::M, BN = Tile<WB>::M;
+    constexpr int TILE_BYTES = Tile<WB>::BYTES;
+    constexpr int LOADS_PER_TILE = Tile<WB>::LOADS;
     // two pipeline stages as distinct objects so the compiler can tell the
     // stage being filled from the stage being read
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * TILE_BYTES];
@@ -124,23 +134,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16*>(p.B + n0 * p.ldb), (short)0, (int)b_bytes, 0x00020000);
 
-    // Wave w fills tile rows [64 w, 64 w + 64) of each operand with 8 loads of
-    // 8 rows; in load q, lane L fills row 64 w + 8 q + L/8 at physical chunk
-    // L % 8, which must hold logical chunk (L % 8) ^ key(row), and
-    // key(row) = (L / 8) ^ (q & 1).
-    const uint32_t lrow = (uint32_t)(w * 64 + (lane >> 3));
+    // Wave w fills tile rows [w BM/4, (w+1) BM/4) of each operand with BM/32
+    // loads of 8 rows; in load q, lane L fills row w BM/4 + 8 q + L/8 at
+    // physical chunk L % 8, which must hold logical chunk (L % 8) ^ key(row),
+    // and key(row) = (L / 8) ^ (q & 1).
+    const uint32_t lrow = (uint32_t)(w * (BM / 4) + (lane >> 3));
     const uint32_t cx0 = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
     const uint32_t cx1 = cx0 ^ 16u;
     const uint32_t a_v0 = lrow * (uint32_t)(p.lda * 2) + cx0, a_v1 = a_v0 - cx0 + cx1;
     const uint32_t b_v0 = lrow * (uint32_t)(p.ldb * 2) + cx0, b_v1 = b_v0 - cx0 + cx1;
     const uint32_t a_qstep = (uint32_t)(8 * p.lda * 2);
     const uint32_t b_qstep = (uint32_t)(8 * p.ldb * 2);
-    const uint32_t dst_w = (uint32_t)(w * 64 * 128);
+    const uint32_t dst_w = (uint32_t)(w * (BM / 4) * 128);
 
     auto load_tile = [&](uint8_t* st, int k0) {
         const uint32_t kb = (uint32_t)k0 * 2u;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < Tile<WB>::QLOADS; ++q) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + dst_w + q * 1024),
                                                      16, (q & 1) ? a_v1 : a_v0, kb + q * a_qstep, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + TILE_BYTES + dst_w + q * 1024),
@@ -153,33 +163,33 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
     // the lane only.
     const uint32_t key = lds_key(lane & 31);
     const int hi = lane >> 5;
-    const uint32_t a_rd = (uint32_t)((wm * 128 + (lane & 31)) * 128);
-    const uint32_t b_rd = (uint32_t)((wn * 128 + (lane & 31)) * 128) + TILE_BYTES;
+    const uint32_t a_rd = (uint32_t)((wm * 32 * WB + (lane & 31)) * 128);
+    const uint32_t b_rd = (uint32_t)((wn * 32 * WB + (lane & 31)) * 128) + TILE_BYTES;
 
-    auto read_frags = [&](const uint8_t* st, int kk, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+    auto read_frags = [&](const uint8_t* st, int kk, bf16x8 (&fa)[WB], bf16x8 (&fb)[WB]) {
         const uint32_t ch = (((uint32_t)(2 * kk + hi)) ^ key) << 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < WB; ++i) {
             fa[i] = *reinterpret_cast<const bf16x8*>(st + a_rd + i * 32 * 128 + ch);
             fb[i] = *reinterpret_cast<const bf16x8*>(st + b_rd + i * 32 * 128 + ch);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[WB][WB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < WB; ++j) acc[i][j] = f32x16{};
 
-    auto mfma16 = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+    auto mfma16 = [&](const bf16x8 (&fa)[WB], const bf16x8 (&fb)[WB]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WB; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < WB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
 
-    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    bf16x8 fa0[WB], fb0[WB], fa1[WB], fb1[WB];
     const int nk = p.K / BK;
     __builtin_assume(nk >= 2);
 
@@ -189,11 +199,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
     // one by one with the current sub-step's MFMAs.
     auto interleave_reads = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 2 * WB; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        if (WB * WB > 2 * WB) __builtin_amdgcn_sched_group_barrier(0x008, WB * WB - 2 * WB, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -219,12 +229,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
             mfma16(fa1, fb1);
             if (do_load) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < 2 * WB; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, Tile<WB>::LOADS / (2 * WB), 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                if (WB * WB > 2 * WB) __builtin_amdgcn_sched_group_barrier(0x008, WB * WB - 2 * WB, 0);
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 interleave_reads();
@@ -266,8 +276,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
     // l % 32 and, in register r, row 8*(r/4) + 4*(l/32) + r%4.
     TC* __restrict__ C = static_cast<TC*>(p.C);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t mb = m0 + wm * 128 + i * 32 + hi * 4;
+    for (int i = 0; i < WB; ++i) {
+        const int64_t mb = m0 + wm * 32 * WB + i * 32 + hi * 4;
         float rs[16], rm[16];
         if constexpr (LN) {
 #pragma unroll
@@ -278,8 +288,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+        for (int j = 0; j < WB; ++j) {
+            const int64_t n = n0 + wn * 32 * WB + j * 32 + (lane & 31);
             float cs = 0.f;
             if constexpr (LN) cs = p.csum[n];
 #pragma unroll
@@ -298,8 +308,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256x256(FastParams p) {
     }
 }
 
-template <int EPI, typename TC>
+template <int WB, int EPI, typename TC>
 hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
+    constexpr int BM = Tile<WB>::M, BN = Tile<WB>::M;
     FastParams p;
     p.A = static_cast<const bf16*>(g.A); p.lda = g.lda;
     p.B = static_cast<const bf16*>(g.B); p.ldb = g.ldb;
@@ -312,11 +323,11 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
     const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n);
     const bool odd = (g.K / BK) & 1;
     if (g.ln_mean) {
-        if (odd) gemm_bf16_256x256<EPI, true, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-        else gemm_bf16_256x256<EPI, true, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+        if (odd) gemm_bf16_mfma<WB, EPI, true, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+        else gemm_bf16_mfma<WB, EPI, true, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
     } else {
-        if (odd) gemm_bf16_256x256<EPI, false, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-        else gemm_bf16_256x256<EPI, false, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+        if (odd) gemm_bf16_mfma<WB, EPI, false, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+        else gemm_bf16_mfma<WB, EPI, false, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
     }
     return hipGetLastError();
 }
@@ -325,28 +336,56 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// The 256x256 kernel takes bf16 operands whose M and N are whole tiles, K a
-// whole number (at least two) of 64-wide steps, 16-byte aligned rows, byte offsets of one
-// 256-row operand tile below 2^31 (buffer offsets), and, with the LayerNorm
-// epilogue, the column sums of Bop.
-GemmPath choose_gemm_path(const GemmArgs& g) {
-    if (g.ab_dtype != kBF16) return kPathGeneric;
-    if (g.M <= 0 || g.N <= 0 || g.K <= 0) return kPathGeneric;
-    if (g.M % BM || g.N % BN || g.K % BK || g.K < 2 * BK) return kPathGeneric;
-    if (g.lda % 8 || g.ldb % 8 || !aligned16(g.A) || !aligned16(g.B)) return kPathGeneric;
-    if ((int64_t)BM * g.lda * 2 >= ((int64_t)1 << 31) || (int64_t)BN * g.ldb * 2 >= ((int64_t)1 << 31))
-        return kPathGeneric;
-    if ((g.M / BM) * (g.N / BN) >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) ||
+// CUs of the current device (queried once; 256 on MI355X).
+static int device_cus() {
+    static int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 256;
+        return n;
+    }();
+    return cus;
+}
+
+// Whether the MFMA kernel can take a shape with tiles of 64*wb rows: bf16
+// operands, M and N whole tiles, K a whole number (at least two) of 64-wide
+// steps, 16-byte aligned rows, one operand tile's byte offsets below 2^31
+// (buffer offsets), and, with the LayerNorm epilogue, the column sums of Bop.
+static bool fits_tile(const GemmArgs& g, int wb) {
+    const int64_t tm = 64 * wb;
+    if (g.ab_dtype != kBF16) return false;
+    if (g.M <= 0 || g.N <= 0 || g.K <= 0) return false;
+    if (g.M % tm || g.N % tm || g.K % BK || g.K < 2 * BK) return false;
+    if (g.lda % 8 || g.ldb % 8 || !aligned16(g.A) || !aligned16(g.B)) return false;
+    if (tm * g.lda * 2 >= ((int64_t)1 << 31) || tm * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
+    if ((g.M / tm) * (g.N / tm) >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) ||
         g.N >= ((int64_t)1 << 31) || g.K >= ((int64_t)1 << 31))
-        return kPathGeneric;
-    if (g.ln_mean && !g.ln_csum) return kPathGeneric;
-    return kPathFastBf16;
+        return false;
+    if (g.ln_mean && !g.ln_csum) return false;
+    return true;
+}
+
+// 256x256 tiles (wb = 4) when they keep at least 3/4 of the CUs busy, else
+// 128x128 tiles (wb = 2, two workgroups per CU); 0 = not for the MFMA kernel.
+static int choose_wb(const GemmArgs& g) {
+    if (fits_tile(g, 4) && (g.M / 256) * (g.N / 256) * 4 >= 3 * (int64_t)device_cus()) return 4;
+    if (fits_tile(g, 2)) return 2;
+    if (fits_tile(g, 4)) return 4;
+    return 0;
+}
+
+GemmPath choose_gemm_path(const GemmArgs& g) { return choose_wb(g) ? kPathFastBf16 : kPathGeneric; }
+
+template <int WB>
+static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
+    if (g.epi == kEpiGelu) return launch_typed<WB, kEpiGelu, bf16>(g, stream);
+    return g.c_dtype == kF32 ? launch_typed<WB, kEpiStore, float>(g, stream)
+                             : launch_typed<WB, kEpiStore, bf16>(g, stream);
 }
 
 hipError_t launch_gemm_bf16_fast(const GemmArgs& g, hipStream_t stream) {
-    if (g.epi == kEpiGelu) return launch_typed<kEpiGelu, bf16>(g, stream);
-    return g.c_dtype == kF32 ? launch_typed<kEpiStore, float>(g, stream)
-                             : launch_typed<kEpiStore, bf16>(g, stream);
+    return choose_wb(g) == 2 ? launch_wb<2>(g, stream) : launch_wb<4>(g, stream);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {

@@ -109,6 +109,9 @@ SHAPES = [
     (257, 129, 384, 4, "bf16"),
     (300, 256, 512, 2, "bf16"),
     (256, 64, 256, 1, "bf16"),
+    (256, 128, 256, 1, "bf16"),     # 256x256 kernel with the minimum K (four steps)
+    (512, 256, 512, 2, "bf16"),     # one steady-state iteration plus the tail
+    (512, 384, 1536, 4, "bf16"),
     (512, 256, 1024, 4, "bf16"),
     (768, 512, 768, 3, "bf16"),
     (1280, 768, 2560, 5, "bf16"),
@@ -158,6 +161,23 @@ def test_workload_large_sampled_rows(name):
     ref = oracle_forward(inp.X[rows], inp.A, inp.B, w.n)
     assert_close(got, ref, "bf16", f"{w.name} rows {len(rows)}")
     assert bool(torch.isfinite(Y).all())
+
+
+def test_wide_output_residual_fp32_sampled_rows():
+    """GEMM2 with 256 output tiles of 256x256 (N = D = 4096), a residual and
+    fp32 output; GEMM1 (N = F = 2048) runs on 128x128 tiles."""
+    M, D, F, n = 4096, 4096, 2048, 2
+    say(f"wide output residual fp32 M={M} D={D} F={F} n={n}")
+    inp = workloads.random_case(M, D, F, seed=21, dtype="bf16")
+    Y, _, _ = _run(inp, n, "bf16", residual=True, out_dtype=torch.float32)
+    rows = sample_rows(M, 24, seed=21)
+    ref = oracle_forward(inp.X[rows], inp.A, inp.B, n, residual=True)
+    got = to_f64(Y[torch.from_numpy(rows).to(Y.device)])
+    assert_close(got, ref, "bf16", "wide output, residual, fp32 out")
+    # the residual must not hide MLP errors: the same rows without it
+    Yn, _, _ = _run(inp, n, "bf16", out_dtype=torch.float32)
+    got = to_f64(Yn[torch.from_numpy(rows).to(Yn.device)])
+    assert_close(got, oracle_forward(inp.X[rows], inp.A, inp.B, n), "bf16", "wide output, no residual")
 
 
 @pytest.mark.parametrize("s", [128, 256, 512])
