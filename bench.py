@@ -30,6 +30,10 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 KERNEL_SOURCES = {"gemm1": "tensor_transformer_mlp_tpmlp_amd/csrc/gemm_bf16.hip",
                   "gemm2": "tensor_transformer_mlp_tpmlp_amd/csrc/gemm_bf16.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+# Copy used to calibrate the HBM byte counters: bf16 -> fp32 conversion of
+# CALIB_ELEMS elements after the caches were flushed; it reads 2 and writes 4
+# bytes per element.
+CALIB_ELEMS = 256 * 1024 * 1024
 
 
 def log(msg: str) -> None:
@@ -84,6 +88,111 @@ def _traffic(workload: str, kernel: str, algorithmic_bytes: float):
     return entry.get("hbm_bytes_per_launch")
 
 
+def copy_calibration() -> None:
+    """A plain copy of known size for calibrating FETCH_SIZE / WRITE_SIZE:
+    flush the caches with 2 GiB of unrelated writes, then convert
+    CALIB_ELEMS bf16 values (512 MiB read) to fp32 (1 GiB written)."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(CALIB_ELEMS, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty(CALIB_ELEMS, dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    flush.fill_(1.0)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst, flush
+    log(f"[bench] copy calibration: {CALIB_ELEMS * 2 >> 20} MiB read, {CALIB_ELEMS * 4 >> 20} MiB written")
+
+
+def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload: str, out_dir: str,
+                       command: str) -> None:
+    """Turn rocprofv3 CSV output (kernel trace + FETCH_SIZE + WRITE_SIZE runs of
+    this bench) into the summaries kept under profiles/."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, pattern):
+        files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+        if not files:
+            raise SystemExit(f"no {pattern} under {d}")
+        with open(files[0]) as f:
+            return list(csv.DictReader(f))
+
+    def kind(name):
+        if "gemm_bf16_mfma" in name:
+            epi = name.split("gemm_bf16_mfma")[1]
+            return "gemm1" if epi.startswith("ILi4ELi0") or epi.startswith("ILi2ELi0") else "gemm2"
+        if "copy" in name or "elementwise" in name:
+            return "copy"
+        return None
+
+    stats = rows(trace_dir, "*kernel_stats.csv")
+    trace = rows(trace_dir, "*kernel_trace.csv")
+    durs = {}
+    for r in trace:
+        k = kind(r["Kernel_Name"])
+        if k in ("gemm1", "gemm2"):
+            durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counter(d, name):
+        per = {}
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != name:
+                continue
+            per.setdefault((kind(r["Kernel_Name"]), r["Kernel_Name"], r["Dispatch_Id"]), 0.0)
+            per[(kind(r["Kernel_Name"]), r["Kernel_Name"], r["Dispatch_Id"])] += float(r["Counter_Value"])
+        return per
+
+    fetch, write = counter(fetch_dir, "FETCH_SIZE"), counter(write_dir, "WRITE_SIZE")
+
+    def calib(per, expected_kib):
+        vals = [v for (k, n, _), v in per.items() if k == "copy" and "bfloat16" in n and "float" in n]
+        vals = [v for v in vals if v > expected_kib / 8]
+        return expected_kib / max(vals) if vals else None
+
+    f_read = calib(fetch, CALIB_ELEMS * 2 / 1024)
+    f_write = calib(write, CALIB_ELEMS * 4 / 1024)
+    with open(os.path.join(ROOT, KERNEL_SOURCES["gemm1"]), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    traffic = {}
+    lines = [f"# rocprofv3 summary: TP-MLP forward, workload {workload}", "",
+             f"command (kernel trace): {command}", "", "## kernel trace (average over dispatches)", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for k in ("gemm1", "gemm2"):
+        d = durs.get(k, [])
+        if d:
+            lines.append(f"| {k} | {len(d)} | {statistics.mean(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+    lines += ["", "all kernels (rocprofv3 --stats):", "", "| name | calls | average ns |", "|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']):.0f} |")
+    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)", "",
+              f"calibration copy: {CALIB_ELEMS * 2 >> 20} MiB read / {CALIB_ELEMS * 4 >> 20} MiB written; "
+              f"scale factors read {f_read}, write {f_write}", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes per launch |", "|---|---|---|---|"]
+    for k in ("gemm1", "gemm2"):
+        fv = [v for (kk, _, _), v in fetch.items() if kk == k]
+        wv = [v for (kk, _, _), v in write.items() if kk == k]
+        if fv and wv and f_read and f_write:
+            b = (statistics.mean(fv) * f_read + statistics.mean(wv) * f_write) * 1024
+            traffic[k] = {"fetch_kib": statistics.mean(fv), "write_kib": statistics.mean(wv),
+                          "hbm_bytes_per_launch": b, "source_sha256": sha}
+            lines.append(f"| {k} | {statistics.mean(fv):.0f} | {statistics.mean(wv):.0f} | {b:.4g} |")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"tpmlp_forward_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allt = json.load(f)
+    except (OSError, ValueError):
+        allt = {}
+    allt[workload] = {"read_scale": f_read, "write_scale": f_write, **traffic}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allt, f, indent=1)
+    print("\n".join(lines))
+
+
 def cpu_baseline(w, inp, target_s: float):
     """The fp64 oracle, untuned, on a bounded row sample of the same workload."""
     import numpy as np
@@ -106,25 +215,39 @@ def cpu_baseline(w, inp, target_s: float):
             oracle.tp_mlp(x, shards)
         return time.perf_counter() - t0
 
-    probe = min(8, w.M)
+    # size the sample from a 64-row probe: the whole workload when it fits the
+    # target time, else a row prefix of about that length
+    probe = min(64, w.M)
     t_probe = run(probe)
-    rows = int(min(w.M, max(probe, probe * target_s / max(t_probe, 1e-6))))
+    est_full = t_probe * w.M / probe
+    rows = w.M if est_full <= target_s else int(max(probe, w.M * target_s / est_full))
     t = run(rows)
     flops = 4.0 * rows * w.D * w.F
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} of {w.M} rows of X (rows are independent), full D={w.D}, F={w.F}, "
-                      f"n={w.n}; numpy fp64, {t:.1f} s"}
+            "sample": (f"all {w.M} rows" if rows == w.M else f"first {rows} of {w.M} rows of X (rows are "
+                       "independent)") + f", D={w.D}, F={w.F}, n={w.n}; numpy fp64 oracle, {t:.1f} s"}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline bf16 size)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run the plain copy used to calibrate the HBM byte counters first")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV output of this bench")
+    ap.add_argument("--profile-command", default="", help="command recorded in the profile summary")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        import workloads
+        summarize_profiles(*args.summarize_profiles, args.workload or workloads.HEADLINE,
+                           os.path.join(ROOT, "profiles"), args.profile_command)
+        return 0
 
     if args.gpus != 1:
         msg = (f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -141,6 +264,8 @@ def main() -> int:
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
+    if args.copy_calibration:
+        copy_calibration()
     dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     log(f"[bench] workload {w.name}: M={w.M} D={w.D} F={w.F} n={w.n} {w.dtype} "
         f"layernorm={w.layernorm} residual={w.residual}")
