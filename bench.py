@@ -218,6 +218,7 @@ def cpu_baseline(w, inp, target_s: float):
     # size the sample from a 64-row probe: the whole workload when it fits the
     # target time, else a row prefix of about that length
     probe = min(64, w.M)
+    run(min(16, w.M))  # warm the BLAS thread pool and the allocator first
     t_probe = run(probe)
     est_full = t_probe * w.M / probe
     rows = w.M if est_full <= target_s else int(max(probe, w.M * target_s / est_full))

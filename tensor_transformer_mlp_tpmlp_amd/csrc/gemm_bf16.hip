@@ -27,13 +27,16 @@
 //
 // Pipeline per K step of tile t (k-sub-steps kk = 0..3, 16 MFMAs each):
 //   kk = 0..2: read the MFMA fragments of kk+1 from LDS while the matrix
-//              cores run kk;
+//              cores run kk; in kk = 0 also issue the second half of tile
+//              t+1's loads;
 //   kk = 3   : wait until this wave's LDS reads and tile t+1's loads have
 //              landed, barrier (tile t+1 visible to all waves, tile t's stage
-//              free), issue tile t+2's loads into the freed stage, read tile
-//              t+1's first fragments, then run kk = 3.
-// So global loads have a whole K step (2048 MFMA cycles) to arrive, LDS reads
-// are always one sub-step ahead, and there is one barrier per K step.
+//              free), issue the first half of tile t+2's loads into the freed
+//              stage, read tile t+1's first fragments, then run kk = 3.
+// Splitting each tile's loads over two sub-steps, one load every few MFMAs,
+// keeps a burst of loads from stalling MFMA issue; the loads still have most
+// of a K step to arrive, LDS reads are always one sub-step ahead, and there is
+// one barrier per K step.
 //
 // LayerNorm prologue (FFN half of the Post-LN block, "LLM Lab Notes 06",
 // section 2, marker 5) is applied algebraically in GEMM1's epilogue:
@@ -72,6 +75,7 @@ struct FastParams {
     const float* rstd;
     const float* csum;   // LayerNorm: per-column sums of Bop (= column sums of A)
     int tiles_m, tiles_n;
+    int nt_store;        // write C with non-temporal stores
 };
 
 // s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
@@ -158,6 +162,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
         }
     };
 
+    auto load_half = [&](uint8_t* st, int k0, int h) {
+        const uint32_t kb = (uint32_t)k0 * 2u;
+#pragma unroll
+        for (int qq = 0; qq < Tile<WB>::QLOADS / 2; ++qq) {
+            const int q = h * (Tile<WB>::QLOADS / 2) + qq;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + dst_w + q * 1024),
+                                                     16, (q & 1) ? a_v1 : a_v0, kb + q * a_qstep, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + TILE_BYTES + dst_w + q * 1024),
+                                                     16, (q & 1) ? b_v1 : b_v0, kb + q * b_qstep, 0, 0);
+        }
+    };
+
     // MFMA operand reads: lane l reads row (l & 31) of each 32-row block at
     // logical chunk 2 kk + (l >> 5); the swizzle key of those rows depends on
     // the lane only.
@@ -209,10 +225,29 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
 
     // One K step on the tile held in `cur`.  has_next: a next tile exists (in
     // `nxt`); do_load: also refill `cur` with the tile two steps ahead.
-    auto k_step = [&](uint8_t* cur, uint8_t* nxt, int k_load, bool has_next, bool do_load) {
+    // 256x256 tiles split each tile's loads over two sub-steps; 128x128 tiles
+    // have four times shorter K steps and issue a tile's loads at once, a full
+    // K step ahead.
+    constexpr bool kSplit = WB >= 4;
+    constexpr int kLoadsPerGroup = Tile<WB>::LOADS / ((kSplit ? 2 : 1) * 2 * WB);
+
+    auto k_step = [&](uint8_t* cur, uint8_t* nxt, int k_load, bool has_next, bool do_load, int k_pend, bool pend) {
+        pend = pend && kSplit;
         read_frags(cur, 1, fa1, fb1);
+        if (pend) load_half(nxt, k_pend, 1);
         mfma16(fa0, fb0);
-        interleave_reads();
+        if (pend) {
+#pragma unroll
+            for (int i = 0; i < 2 * WB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerGroup, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if (WB * WB > 2 * WB) __builtin_amdgcn_sched_group_barrier(0x008, WB * WB - 2 * WB, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            interleave_reads();
+        }
         read_frags(cur, 2, fa0, fb0);
         mfma16(fa1, fb1);
         interleave_reads();
@@ -224,14 +259,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            if (do_load) load_tile(cur, k_load);
+            if (do_load) {
+                if constexpr (kSplit) load_half(cur, k_load, 0);
+                else load_tile(cur, k_load);
+            }
             read_frags(nxt, 0, fa0, fb0);
             mfma16(fa1, fb1);
             if (do_load) {
 #pragma unroll
                 for (int i = 0; i < 2 * WB; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, Tile<WB>::LOADS / (2 * WB), 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerGroup, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
                 if (WB * WB > 2 * WB) __builtin_amdgcn_sched_group_barrier(0x008, WB * WB - 2 * WB, 0);
@@ -244,32 +282,33 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
         }
     };
 
+    // prologue: step 0 whole and the first half of step 1 (all of step 1
+    // without the split); wait for step 0
     load_tile(stage0, 0);
-    if (nk > 1) {
+    if constexpr (kSplit) {
+        load_half(stage1, BK, 0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_TILE / 2));
+    } else {
         load_tile(stage1, BK);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_TILE));
-    } else {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
     __builtin_amdgcn_s_barrier();
     read_frags(stage0, 0, fa0, fb0);
 
-    // Steady state, branch-free: tiles kt (stage 0) and kt+1 (stage 1), each
-    // refilling its stage with the tile two ahead.
+    // step t issues the second half of step t+1 (kk0) and the first half of
+    // t+2 (kk3); without the split, all of t+2 at kk3
     int kt = 0;
     for (; kt + 3 < nk; kt += 2) {
-        k_step(stage0, stage1, (kt + 2) * BK, true, true);
-        k_step(stage1, stage0, (kt + 3) * BK, true, true);
+        k_step(stage0, stage1, (kt + 2) * BK, true, true, (kt + 1) * BK, true);
+        k_step(stage1, stage0, (kt + 3) * BK, true, true, (kt + 2) * BK, true);
     }
-    // The last two (even step count) or three (odd) tiles, as straight-line
-    // code: one tail shape per instantiation keeps the accumulators in AGPRs.
     if constexpr (ODD) {
-        k_step(stage0, stage1, (kt + 2) * BK, true, true);
-        k_step(stage1, stage0, 0, true, false);
-        k_step(stage0, stage1, 0, false, false);
+        k_step(stage0, stage1, (kt + 2) * BK, true, true, (kt + 1) * BK, true);
+        k_step(stage1, stage0, 0, true, false, (kt + 2) * BK, true);
+        k_step(stage0, stage1, 0, false, false, 0, false);
     } else {
-        k_step(stage0, stage1, 0, true, false);
-        k_step(stage1, stage0, 0, false, false);
+        k_step(stage0, stage1, 0, true, false, (kt + 1) * BK, true);
+        k_step(stage1, stage0, 0, false, false, 0, false);
     }
 
     // Epilogue.  Accumulator layout of a 32x32 MFMA: lane l holds column
@@ -302,7 +341,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
                 } else {
                     if (p.R) v += static_cast<float>(p.R[m * p.ldr + n]);
                 }
-                C[m * p.ldc + n] = from_f32<TC>(v);
+                // A large output (H of the big workloads) is written
+                // non-temporally: it would not fit the caches anyway, and
+                // keeping it out of them keeps the operands resident in the
+                // Infinity Cache.  A small one stays cached for its reader.
+                if (p.nt_store)
+                    __builtin_nontemporal_store(from_f32<TC>(v), &C[m * p.ldc + n]);
+                else
+                    C[m * p.ldc + n] = from_f32<TC>(v);
             }
         }
     }
@@ -320,6 +366,7 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
     p.mean = g.ln_mean; p.rstd = g.ln_rstd; p.csum = g.ln_csum;
     p.tiles_m = (int)(g.M / BM);
     p.tiles_n = (int)(g.N / BN);
+    p.nt_store = g.M * g.N * (int64_t)sizeof(TC) > ((int64_t)128 << 20);
     const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n);
     const bool odd = (g.K / BK) & 1;
     if (g.ln_mean) {
