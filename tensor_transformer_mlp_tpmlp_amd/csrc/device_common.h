@@ -20,13 +20,17 @@ constexpr float kGeluA = 0.044715f;
 
 // GeLU_tanh(x) = x/2 (1 + tanh u), u = sqrt(2/pi) (x + 0.044715 x^3).
 // Evaluated as x * sigmoid(2u) = x / (1 + exp(-2u)), which is the same
-// function since (1 + tanh u)/2 = 1/(1 + exp(-2u)).  One v_exp_f32 and one
-// v_rcp_f32.  exp(-2u) overflows to +inf for very negative x, giving -0; it
+// function since (1 + tanh u)/2 = 1/(1 + exp(-2u)).  With exp(-2u) =
+// 2^(x (k0 + k1 x^2)), k0 = -2 sqrt(2/pi) log2(e) and k1 = 0.044715 k0, that
+// is two multiplies, one fma, one v_exp_f32, one add, one v_rcp_f32 and one
+// multiply.  2^(...) overflows to +inf for very negative x, giving -0; it
 // underflows to 0 for large x, giving x.  NaN propagates.
+constexpr double kLog2e = 1.4426950408889634;
+constexpr float kGeluK0 = (float)(-2.0 * (double)kGeluC * kLog2e);
+constexpr float kGeluK1 = (float)(-2.0 * (double)kGeluC * (double)kGeluA * kLog2e);
 __device__ __forceinline__ float gelu_tanh(float x) {
-    const float u2 = -2.0f * kGeluC * x * __builtin_fmaf(kGeluA * x, x, 1.0f);
-    const float e = __builtin_amdgcn_exp2f(u2 * 1.4426950408889634f);  // exp(u2)
-    return x * __builtin_amdgcn_rcpf(1.0f + e);
+    const float z = x * __builtin_fmaf(x * x, kGeluK1, kGeluK0);
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
 __device__ __forceinline__ float to_f32(float v) { return v; }

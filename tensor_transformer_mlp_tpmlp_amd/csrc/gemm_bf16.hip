@@ -1,7 +1,7 @@
 // Throughput GEMM for bf16 operands on gfx950 matrix cores.
 //
 // C[m][n] = epi( sum_k Aop[m][k] * Bop[n][k] ), Aop (M x K) and Bop (N x K)
-// K-contiguous, fp32 accumulation in v_mfma_f32_32x32x16_bf16.
+// K-contiguous, fp32 accumulation in v_mfma_f32_16x16x32_bf16.
 //
 // Both GEMMs of the TP-MLP run here:
 //   * column-parallel GEMM1 ("Tensor-Parallel MLP (Megatron)", section
@@ -14,29 +14,32 @@
 //     the chip.
 //
 // Tiling: one 256x256 output tile per workgroup of 4 waves (2x2, one wave per
-// SIMD), each wave owning a 128x128 sub-tile: 4x4 MFMA 32x32 blocks, 256 fp32
-// accumulators per lane held in AGPRs.  Shapes too small to fill the GPU with
-// 256x256 tiles use 128x128 tiles (2x2 blocks per wave, 64 KiB of LDS, two
-// workgroups per CU) with the same pipeline.  K advances in steps of 64 through two
-// LDS stages of 64 KiB (A tile 32 KiB + B tile 32 KiB).
+// SIMD), each wave owning a 128x128 sub-tile: 8x8 MFMA blocks of 16x16, 256
+// fp32 accumulators per lane held in AGPRs.  Shapes too small to fill the GPU
+// with 256x256 tiles use 128x128 tiles (4x4 blocks per wave, 80 KiB of LDS,
+// two workgroups per CU) with the same pipeline.  K advances 64 per step;
+// each operand's 64-wide slice of a step is a "unit" (32 KiB at 256x256),
+// and a ring of five unit slots fills the 160 KiB of LDS.
+//
+// The 16x16x32 MFMA is used rather than 32x32x16: with random operands it
+// sustains a higher clock under the chip's power limit for the same FLOP.
+// Each MFMA takes the Bop fragment as its first operand, so a lane's four
+// accumulators are four consecutive output columns of one row: the epilogue
+// writes 8 (bf16) or 16 (fp32) contiguous bytes per lane and block.
 //
 // Global -> LDS moves use the direct-to-LDS buffer load (buffer_load_dwordx4
 // ... lds): no VGPR staging and no ds_write.  Lane L of a wave's load lands at
 // LDS base + 16 L, so the XOR swizzle of the LDS layout is applied on the
 // global side by choosing which 16-byte chunk each lane fetches.
 //
-// Pipeline per K step of tile t (k-sub-steps kk = 0..3, 16 MFMAs each):
-//   kk = 0..2: read the MFMA fragments of kk+1 from LDS while the matrix
-//              cores run kk; in kk = 0 also issue the second half of tile
-//              t+1's loads;
-//   kk = 3   : wait until this wave's LDS reads and tile t+1's loads have
-//              landed, barrier (tile t+1 visible to all waves, tile t's stage
-//              free), issue the first half of tile t+2's loads into the freed
-//              stage, read tile t+1's first fragments, then run kk = 3.
-// Splitting each tile's loads over two sub-steps, one load every few MFMAs,
-// keeps a burst of loads from stalling MFMA issue; the loads still have most
-// of a K step to arrive, LDS reads are always one sub-step ahead, and there is
-// one barrier per K step.
+// Pipeline: step t computes two 32-deep sub-steps from units A_t and B_t.
+// Sub-step 0 reads the fragments of sub-step 1 and issues the loads of
+// A_{t+2}; a barrier then publishes A_{t+1}, B_{t+1} and frees A_t, B_t;
+// sub-step 1 reads the next step's first fragments and issues B_{t+2} into
+// A_t's slot.  Each load covers whole 128-byte lines (8 rows x 128 bytes),
+// the unit the L1 fetches from L2 in, so a step costs the CU's load path the
+// fewest requests; loads and reads are spread evenly between the MFMAs.  A
+// load of B has more than one sub-step, a load of A more than two, to land.
 //
 // LayerNorm prologue (FFN half of the Post-LN block, "LLM Lab Notes 06",
 // section 2, marker 5) is applied algebraically in GEMM1's epilogue:
@@ -46,19 +49,24 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace tpmlp {
 
 namespace {
 
-// WB = MFMA blocks of 32x32 per wave per side: 4 gives the 256x256 tile
-// (128x128 per wave), 2 the 128x128 tile (64x64 per wave) used when 256x256
-// tiles would leave CUs idle.
+// WB: the tile is 64*WB square; 4 gives 256x256 (128x128 per wave), 2 gives
+// 128x128 (64x64 per wave), used when 256x256 tiles would leave CUs idle.
+// K advances BK = 64 per step, two 16x16x32 MFMA sub-steps.  The operands
+// of a step live in LDS as two "units", one per operand (M rows of 128
+// bytes), in a ring of NUNIT unit slots.
 constexpr int BK = 64;
+constexpr int NUNIT = 5;
 template <int WB> struct Tile {
-    static constexpr int M = 64 * WB;         // tile rows (= tile columns)
-    static constexpr int BYTES = M * BK * 2;  // one operand tile of one stage
-    static constexpr int QLOADS = M / 32;     // direct loads per wave per operand per K step
-    static constexpr int LOADS = 2 * QLOADS;  // per wave per K step
+    static constexpr int M = 64 * WB;             // tile rows (= tile columns)
+    static constexpr int UNIT_BYTES = M * BK * 2;  // one operand of one step
+    static constexpr int NB = 2 * WB;             // 16x16 MFMA blocks per wave per side
+    static constexpr int LPU = M / 32;            // direct loads per wave per unit
 };
 
 struct FastParams {
@@ -75,6 +83,7 @@ struct FastParams {
     const float* rstd;
     const float* csum;   // LayerNorm: per-column sums of Bop (= column sums of A)
     int tiles_m, tiles_n;
+    int group;           // tile rows walked together on one XCD
     int nt_store;        // write C with non-temporal stores
 };
 
@@ -83,54 +92,93 @@ struct FastParams {
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
 
-// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row` in LDS.  The
-// XOR key (row & 7) ^ ((row >> 3) & 1) puts any 8 consecutive rows, and the
-// even and the odd rows of any 16 consecutive rows, on distinct chunks, which
-// keeps 128-bit accesses conflict-free whether the LDS serves 8 or 16 lanes
-// per cycle.
-__device__ __forceinline__ uint32_t lds_key(int row) { return (uint32_t)((row & 7) ^ ((row >> 3) & 1)); }
+// LDS layout of a unit: tile row r at byte 128 r, its eight 16-byte
+// k-chunks permuted: logical chunk c sits at physical chunk c ^ key(r),
+// key(r) = ((r & 8) >> 2) | ((r & 2) << 1).  A 128-bit LDS read is served
+// in four passes of 16 lanes; within each half-wave, the 4-lane groups whose
+// index (0..7) has an even number of set bits form one pass and the others
+// the second (measured with the bank-conflict counter).  A fragment read puts
+// rows j, j+12 of one chunk and rows j+4, j+8 of the next into one pass; the
+// key sends the sixteen lanes of every pass to distinct 16-byte bank groups,
+// so the reads are conflict-free.  The direct loads write 1 KiB contiguously,
+// which is conflict-free under any key.
+__device__ __forceinline__ uint32_t lds_key(uint32_t r) { return ((r & 8) >> 2) | ((r & 2) << 1); }
 
 // Blocks reach the 8 XCDs round-robin (block b runs on XCD b % 8).  Give each
-// XCD a contiguous range of tile ids, and walk that range in groups of 8 tile
-// rows so that concurrently running tiles share A rows and B columns in the
-// XCD's L2.  Bijective for any tile count.
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+// XCD a contiguous range of tile ids, and walk that range in groups of
+// `group` tile rows, column by column, so that the tiles running at once on
+// an XCD share Aop rows and Bop columns in its L2.  Bijective for any tile
+// count and group.
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int group, int& tm, int& tn) {
     const int total = tiles_m * tiles_n;
     const int xcd = bid & 7, idx = bid >> 3;
     const int per = total >> 3, rem = total & 7;
     const int pid = xcd * per + min(xcd, rem) + idx;
-    constexpr int GROUP = 8;
-    const int group_tiles = GROUP * tiles_n;
+    const int group_tiles = group * tiles_n;
     const int g = pid / group_tiles;
-    const int first_m = g * GROUP;
-    const int gm = min(tiles_m - first_m, GROUP);
+    const int first_m = g * group;
+    const int gm = min(tiles_m - first_m, group);
     const int local = pid - g * group_tiles;
     tm = first_m + local % gm;
     tn = local / gm;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-template <int WB, int EPI, bool LN, bool ODD, typename TC>
+template <int V> using ic = std::integral_constant<int, V>;
+
+// gelu_tanh of N f32x4 values, one operation of the formula at a time over
+// all of them (the same operations as gelu_tanh, so the same results).  The
+// scheduling barriers keep the compiler from evaluating the values one
+// after another, which would expose the latency of every step.
+template <int N>
+__device__ __forceinline__ void gelu_tanh_staged(f32x4 (&v)[N]) {
+    f32x4 z[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[j][r] = v[j][r] * v[j][r];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[j][r] = v[j][r] * __builtin_fmaf(z[j][r], kGeluK1, kGeluK0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[j][r] = __builtin_amdgcn_exp2f(z[j][r]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[j][r] = __builtin_amdgcn_rcpf(1.0f + z[j][r]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[j][r] = v[j][r] * z[j][r];
+}
+
+template <int WB, int EPI, bool LN, typename TC>
 __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     constexpr int BM = Tile<WB>::M, BN = Tile<WB>::M;
-    constexpr int TILE_BYTES = Tile<WB>::BYTES;
-    constexpr int LOADS_PER_TILE = Tile<WB>::LOADS;
-    // two pipeline stages as distinct objects so the compiler can tell the
-    // stage being filled from the stage being read
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[2 * TILE_BYTES];
+    constexpr int NB = Tile<WB>::NB;
+    constexpr int UB = Tile<WB>::UNIT_BYTES;
+    constexpr int LPU = Tile<WB>::LPU;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NUNIT * UB];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, kept in an SGPR
     const int wm = w >> 1, wn = w & 1;
     int tm, tn;
-    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
 
-    // Buffer resources over this tile's 256 rows of each operand.
+    // Buffer resources over this tile's rows of each operand.
     const uint32_t a_bytes = (uint32_t)(BM * p.lda * 2);
     const uint32_t b_bytes = (uint32_t)(BN * p.ldb * 2);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
@@ -138,217 +186,215 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16*>(p.B + n0 * p.ldb), (short)0, (int)b_bytes, 0x00020000);
 
-    // Wave w fills tile rows [w BM/4, (w+1) BM/4) of each operand with BM/32
-    // loads of 8 rows; in load q, lane L fills row w BM/4 + 8 q + L/8 at
-    // physical chunk L % 8, which must hold logical chunk (L % 8) ^ key(row),
-    // and key(row) = (L / 8) ^ (q & 1).
+    // Wave w fills rows [w BM/4, (w+1) BM/4) of a unit with LPU loads of 8
+    // rows (1 KiB); in load q, lane L fills row w BM/4 + 8 q + L/8 at physical
+    // chunk L % 8, which must hold logical chunk (L % 8) ^ key(row), and
+    // row % 16 = 8 (q & 1) + L/8 since BM/4 is a multiple of 16.
     const uint32_t lrow = (uint32_t)(w * (BM / 4) + (lane >> 3));
-    const uint32_t cx0 = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
-    const uint32_t cx1 = cx0 ^ 16u;
+    const uint32_t cx0 = ((uint32_t)(lane & 7) ^ lds_key((uint32_t)lane >> 3)) << 4;
+    const uint32_t cx1 = ((uint32_t)(lane & 7) ^ lds_key(8u + ((uint32_t)lane >> 3))) << 4;
     const uint32_t a_v0 = lrow * (uint32_t)(p.lda * 2) + cx0, a_v1 = a_v0 - cx0 + cx1;
     const uint32_t b_v0 = lrow * (uint32_t)(p.ldb * 2) + cx0, b_v1 = b_v0 - cx0 + cx1;
     const uint32_t a_qstep = (uint32_t)(8 * p.lda * 2);
     const uint32_t b_qstep = (uint32_t)(8 * p.ldb * 2);
     const uint32_t dst_w = (uint32_t)(w * (BM / 4) * 128);
 
-    auto load_tile = [&](uint8_t* st, int k0) {
+    // slot s of the ring
+    auto slot = [&](int s) { return ring + s * UB; };
+
+    // load q of the unit of operand `op` (0 = Aop, 1 = Bop) at k0 into slot st
+    auto load_one = [&](uint8_t* st, int op, int k0, int q) {
         const uint32_t kb = (uint32_t)k0 * 2u;
+        if (op)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + dst_w + q * 1024), 16,
+                                                     (q & 1) ? b_v1 : b_v0, kb + q * b_qstep, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + dst_w + q * 1024), 16,
+                                                     (q & 1) ? a_v1 : a_v0, kb + q * a_qstep, 0, 0);
+    };
+    auto load_unit = [&](uint8_t* st, int op, int k0) {
 #pragma unroll
-        for (int q = 0; q < Tile<WB>::QLOADS; ++q) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + dst_w + q * 1024),
-                                                     16, (q & 1) ? a_v1 : a_v0, kb + q * a_qstep, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + TILE_BYTES + dst_w + q * 1024),
-                                                     16, (q & 1) ? b_v1 : b_v0, kb + q * b_qstep, 0, 0);
+        for (int q = 0; q < LPU; ++q) load_one(st, op, k0, q);
+    };
+
+    // MFMA operand reads: a 16x16x32 fragment is 16 rows x 32 k; in sub-step
+    // kk lane l reads row (l & 15) of the block at logical chunk
+    // 4 kk + (l >> 4).  The same lane -> k assignment for both operands makes
+    // each MFMA a plain 32-long dot product per output.
+    const uint32_t kr = lds_key((uint32_t)lane & 15);
+    const uint32_t rd_a = (uint32_t)((wm * 16 * NB + (lane & 15)) * 128);
+    const uint32_t rd_b = (uint32_t)((wn * 16 * NB + (lane & 15)) * 128);
+    const uint32_t ch0 = (((uint32_t)(lane >> 4)) ^ kr) << 4;
+    const uint32_t ch1 = (((uint32_t)(4 + (lane >> 4))) ^ kr) << 4;
+
+    // acc[i][j]: Aop block i (rows), Bop block j (columns).  With the Bop
+    // fragment first, lane l holds row (l & 15) of block i and columns
+    // 4 (l >> 4) + r, r = 0..3, of block j.  The MFMAs are issued as inline
+    // assembly with the accumulator tied to AGPRs ("+a"): the compiler keeps
+    // every accumulator in place for the whole K loop (its own MFMA builtin
+    // lets the register allocator move some of 256 live accumulators between
+    // AGPRs and VGPRs), and the order of MFMAs, LDS reads and direct loads
+    // within a sub-step is the order written below.  The two hazards it no
+    // longer sees are covered explicitly: the AGPR writes of the zero
+    // initialisation before the first MFMA reads them, and the last MFMA's
+    // results before the epilogue reads them.
+    f32x4 acc[NB][NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            acc[i][j] = f32x4{};
+            asm volatile("" : "+a"(acc[i][j]));
         }
-    };
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 
-    auto load_half = [&](uint8_t* st, int k0, int h) {
-        const uint32_t kb = (uint32_t)k0 * 2u;
-#pragma unroll
-        for (int qq = 0; qq < Tile<WB>::QLOADS / 2; ++qq) {
-            const int q = h * (Tile<WB>::QLOADS / 2) + qq;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + dst_w + q * 1024),
-                                                     16, (q & 1) ? a_v1 : a_v0, kb + q * a_qstep, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + TILE_BYTES + dst_w + q * 1024),
-                                                     16, (q & 1) ? b_v1 : b_v0, kb + q * b_qstep, 0, 0);
-        }
-    };
-
-    // MFMA operand reads: lane l reads row (l & 31) of each 32-row block at
-    // logical chunk 2 kk + (l >> 5); the swizzle key of those rows depends on
-    // the lane only.
-    const uint32_t key = lds_key(lane & 31);
-    const int hi = lane >> 5;
-    const uint32_t a_rd = (uint32_t)((wm * 32 * WB + (lane & 31)) * 128);
-    const uint32_t b_rd = (uint32_t)((wn * 32 * WB + (lane & 31)) * 128) + TILE_BYTES;
-
-    auto read_frags = [&](const uint8_t* st, int kk, bf16x8 (&fa)[WB], bf16x8 (&fb)[WB]) {
-        const uint32_t ch = (((uint32_t)(2 * kk + hi)) ^ key) << 4;
-#pragma unroll
-        for (int i = 0; i < WB; ++i) {
-            fa[i] = *reinterpret_cast<const bf16x8*>(st + a_rd + i * 32 * 128 + ch);
-            fb[i] = *reinterpret_cast<const bf16x8*>(st + b_rd + i * 32 * 128 + ch);
-        }
-    };
-
-    f32x16 acc[WB][WB];
-#pragma unroll
-    for (int i = 0; i < WB; ++i)
-#pragma unroll
-        for (int j = 0; j < WB; ++j) acc[i][j] = f32x16{};
-
-    auto mfma16 = [&](const bf16x8 (&fa)[WB], const bf16x8 (&fb)[WB]) {
-#pragma unroll
-        for (int i = 0; i < WB; ++i)
-#pragma unroll
-            for (int j = 0; j < WB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    };
-
-    bf16x8 fa0[WB], fb0[WB], fa1[WB], fb1[WB];
+    bf16x8 fa0[NB], fb0[NB], fa1[NB], fb1[NB];
     const int nk = p.K / BK;
-    __builtin_assume(nk >= 2);
+    __builtin_assume(nk >= 3);
 
-    // Instruction order inside a K step is pinned with scheduling groups
-    // (mask 0x008 = MFMA, 0x100 = LDS read, 0x020 = VMEM read): the LDS reads
-    // of the next sub-step, and the next tile's global loads, are interleaved
-    // one by one with the current sub-step's MFMAs.
-    auto interleave_reads = [&]() {
-#pragma unroll
-        for (int i = 0; i < 2 * WB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        if (WB * WB > 2 * WB) __builtin_amdgcn_sched_group_barrier(0x008, WB * WB - 2 * WB, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
+    // Per sub-step: NM MFMAs; the NR fragment reads of the next sub-step go
+    // one after every RS-th MFMA from the first, the LPU direct loads of one
+    // unit one after every LS-th.
+    constexpr int NM = NB * NB, NR = 2 * NB, RS = NM / NR / 2 > 0 ? NM / NR / 2 : 1;
+    constexpr int LS = NM / LPU;
+    static_assert(NM % LPU == 0 && (NR - 1) * RS < NM, "sub-step layout");
 
-    // One K step on the tile held in `cur`.  has_next: a next tile exists (in
-    // `nxt`); do_load: also refill `cur` with the tile two steps ahead.
-    // 256x256 tiles split each tile's loads over two sub-steps; 128x128 tiles
-    // have four times shorter K steps and issue a tile's loads at once, a full
-    // K step ahead.
-    constexpr bool kSplit = WB >= 4;
-    constexpr int kLoadsPerGroup = Tile<WB>::LOADS / ((kSplit ? 2 : 1) * 2 * WB);
-
-    auto k_step = [&](uint8_t* cur, uint8_t* nxt, int k_load, bool has_next, bool do_load, int k_pend, bool pend) {
-        pend = pend && kSplit;
-        read_frags(cur, 1, fa1, fb1);
-        if (pend) load_half(nxt, k_pend, 1);
-        mfma16(fa0, fb0);
-        if (pend) {
+    // One sub-step: MFMAs on (fc, gc); read the next fragments at chunk
+    // offset ch from units ua (Aop) and ub (Bop) into (fn, gn); when
+    // `load_op` >= 0, issue the unit of operand load_op at k_load into slot
+    // `dst`.
+    auto sub_step = [&](const bf16x8 (&fc)[NB], const bf16x8 (&gc)[NB], const uint8_t* ua, const uint8_t* ub,
+                        uint32_t ch, bf16x8 (&fn)[NB], bf16x8 (&gn)[NB], bool do_read, uint8_t* dst, int load_op,
+                        int k_load) {
+        const uint8_t* pa = ua + rd_a + ch;
+        const uint8_t* pb = ub + rd_b + ch;
 #pragma unroll
-            for (int i = 0; i < 2 * WB; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerGroup, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int idx = 0; idx < NM; ++idx) {
+            const int i = idx / NB, j = idx % NB;
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(gc[j]), "v"(fc[i]));
+            if (do_read && idx % RS == 0 && idx / RS < NR) {
+                // fragment reads in consumption order: Aop 0, Bop 0..NB-1, Aop 1..NB-1
+                const int r = idx / RS;
+                if (r == 0) fn[0] = *reinterpret_cast<const bf16x8*>(pa);
+                else if (r <= NB) gn[r - 1] = *reinterpret_cast<const bf16x8*>(pb + (r - 1) * 2048);
+                else fn[r - NB] = *reinterpret_cast<const bf16x8*>(pa + (r - NB) * 2048);
             }
-            if (WB * WB > 2 * WB) __builtin_amdgcn_sched_group_barrier(0x008, WB * WB - 2 * WB, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        } else {
-            interleave_reads();
-        }
-        read_frags(cur, 2, fa0, fb0);
-        mfma16(fa1, fb1);
-        interleave_reads();
-        read_frags(cur, 3, fa1, fb1);
-        mfma16(fa0, fb0);
-        interleave_reads();
-        if (has_next) {
-            __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            if (do_load) {
-                if constexpr (kSplit) load_half(cur, k_load, 0);
-                else load_tile(cur, k_load);
-            }
-            read_frags(nxt, 0, fa0, fb0);
-            mfma16(fa1, fb1);
-            if (do_load) {
-#pragma unroll
-                for (int i = 0; i < 2 * WB; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerGroup, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                if (WB * WB > 2 * WB) __builtin_amdgcn_sched_group_barrier(0x008, WB * WB - 2 * WB, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            } else {
-                interleave_reads();
-            }
-        } else {
-            mfma16(fa1, fb1);
+            if (load_op >= 0 && idx % LS == 0) load_one(dst, load_op, k_load, idx / LS);
         }
     };
 
-    // prologue: step 0 whole and the first half of step 1 (all of step 1
-    // without the split); wait for step 0
-    load_tile(stage0, 0);
-    if constexpr (kSplit) {
-        load_half(stage1, BK, 0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_TILE / 2));
-    } else {
-        load_tile(stage1, BK);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_TILE));
-    }
+    // Step t reads units A_t, B_t (ring slots 2t, 2t+1 mod NUNIT).  Sub-step
+    // 0 issues A_{t+2} into the slot of B_{t-1}; the barrier between the
+    // sub-steps publishes A_{t+1}, B_{t+1} and frees A_t, B_t; sub-step 1
+    // issues B_{t+2} into the slot of A_t.  A load of B has more than one
+    // sub-step, a load of A more than two, to land before the barrier that
+    // publishes it.
+    auto next = [](int s, int d) { s += d; return s >= NUNIT ? s - NUNIT : s; };
+    auto barrier_wait = [&](auto vm_left) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(decltype(vm_left)::value));
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // prologue: units A_0, B_0, A_1, B_1, A_2 into slots 0..4; wait for step 0
+    load_unit(slot(0), 0, 0);
+    load_unit(slot(1), 1, 0);
+    load_unit(slot(2), 0, BK);
+    load_unit(slot(3), 1, BK);
+    load_unit(slot(4), 0, 2 * BK);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LPU));
     __builtin_amdgcn_s_barrier();
-    read_frags(stage0, 0, fa0, fb0);
-
-    // step t issues the second half of step t+1 (kk0) and the first half of
-    // t+2 (kk3); without the split, all of t+2 at kk3
-    int kt = 0;
-    for (; kt + 3 < nk; kt += 2) {
-        k_step(stage0, stage1, (kt + 2) * BK, true, true, (kt + 1) * BK, true);
-        k_step(stage1, stage0, (kt + 3) * BK, true, true, (kt + 2) * BK, true);
-    }
-    if constexpr (ODD) {
-        k_step(stage0, stage1, (kt + 2) * BK, true, true, (kt + 1) * BK, true);
-        k_step(stage1, stage0, 0, true, false, (kt + 2) * BK, true);
-        k_step(stage0, stage1, 0, false, false, 0, false);
-    } else {
-        k_step(stage0, stage1, 0, true, false, (kt + 1) * BK, true);
-        k_step(stage1, stage0, 0, false, false, 0, false);
+    {
+        const uint8_t* pa = slot(0) + rd_a + ch0;
+        const uint8_t* pb = slot(1) + rd_b + ch0;
+        fa0[0] = *reinterpret_cast<const bf16x8*>(pa);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fb0[j] = *reinterpret_cast<const bf16x8*>(pb + j * 2048);
+#pragma unroll
+        for (int i = 1; i < NB; ++i) fa0[i] = *reinterpret_cast<const bf16x8*>(pa + i * 2048);
     }
 
-    // Epilogue.  Accumulator layout of a 32x32 MFMA: lane l holds column
-    // l % 32 and, in register r, row 8*(r/4) + 4*(l/32) + r%4.
+    // step 0: A_2 is already in flight
+    sub_step(fa0, fb0, slot(0), slot(1), ch1, fa1, fb1, true, nullptr, -1, 0);
+    barrier_wait(ic<LPU>{});
+    sub_step(fa1, fb1, slot(2), slot(3), ch0, fa0, fb0, true, slot(0), 1, 2 * BK);
+
+    // steps 1 .. nk-3
+    int sa = 2;  // slot of A_t
+    for (int kt = 1; kt + 2 < nk; ++kt) {
+        const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3), sa2 = next(sa, 4);
+        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, fa1, fb1, true, slot(sa2), 0, (kt + 2) * BK);
+        barrier_wait(ic<LPU>{});
+        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, fa0, fb0, true, slot(sa), 1, (kt + 2) * BK);
+        sa = sa1;
+    }
+    // step nk-2: nothing left to load
+    {
+        const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3);
+        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, fa1, fb1, true, nullptr, -1, 0);
+        barrier_wait(ic<0>{});
+        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, fa0, fb0, true, nullptr, -1, 0);
+        sa = sa1;
+    }
+    // step nk-1
+    sub_step(fa0, fb0, slot(sa), slot(next(sa, 1)), ch1, fa1, fb1, true, nullptr, -1, 0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+    sub_step(fa1, fb1, slot(sa), slot(sa), ch0, fa0, fb0, false, nullptr, -1, 0);
+    // results of the last MFMAs are read by the epilogue
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // Epilogue: lane l writes row m = ... + (l & 15) of block i, columns
+    // n .. n+3 with n = ... + 4 (l >> 4) of block j.  A whole row block is
+    // transformed before it is stored, which gives the scheduler NB * 4
+    // independent GeLU chains to interleave.
     TC* __restrict__ C = static_cast<TC*>(p.C);
+    const int64_t n_base = n0 + wn * 16 * NB + 4 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < WB; ++i) {
-        const int64_t mb = m0 + wm * 32 * WB + i * 32 + hi * 4;
-        float rs[16], rm[16];
+    for (int i = 0; i < NB; ++i) {
+        const int64_t m = m0 + wm * 16 * NB + i * 16 + (lane & 15);
+        f32x4 v[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) v[j] = acc[i][j];
         if constexpr (LN) {
+            const float rs = p.rstd[m];
+            const float rm = rs * p.mean[m];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = mb + (r >> 2) * 8 + (r & 3);
-                rs[r] = p.rstd[m];
-                rm[r] = rs[r] * p.mean[m];
+            for (int j = 0; j < NB; ++j) {
+                const f32x4 cs = *reinterpret_cast<const f32x4*>(p.csum + n_base + j * 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[j][r] = __builtin_fmaf(rs, v[j][r], -rm * cs[r]);
             }
         }
+        if constexpr (EPI == kEpiGelu) {
+            gelu_tanh_staged(v);
+        } else {
+            if (p.R) {
 #pragma unroll
-        for (int j = 0; j < WB; ++j) {
-            const int64_t n = n0 + wn * 32 * WB + j * 32 + (lane & 31);
-            float cs = 0.f;
-            if constexpr (LN) cs = p.csum[n];
+                for (int j = 0; j < NB; ++j) {
+                    const bf16x4 rv = *reinterpret_cast<const bf16x4*>(p.R + m * p.ldr + n_base + j * 16);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = mb + (r >> 2) * 8 + (r & 3);
-                float v = acc[i][j][r];
-                if constexpr (LN) v = __builtin_fmaf(rs[r], v, -rm[r] * cs);
-                if constexpr (EPI == kEpiGelu) {
-                    v = gelu_tanh(v);
-                } else {
-                    if (p.R) v += static_cast<float>(p.R[m * p.ldr + n]);
+                    for (int r = 0; r < 4; ++r) v[j][r] += static_cast<float>(rv[r]);
                 }
-                // A large output (H of the big workloads) is written
-                // non-temporally: it would not fit the caches anyway, and
-                // keeping it out of them keeps the operands resident in the
-                // Infinity Cache.  A small one stays cached for its reader.
-                if (p.nt_store)
-                    __builtin_nontemporal_store(from_f32<TC>(v), &C[m * p.ldc + n]);
-                else
-                    C[m * p.ldc + n] = from_f32<TC>(v);
+            }
+        }
+        // A large output (H of the big workloads) is written non-temporally:
+        // it would not fit the caches anyway, and keeping it out of them
+        // keeps the operands resident in the Infinity Cache.  A small one
+        // stays cached for its reader.
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            TC* row = C + m * p.ldc + n_base + j * 16;
+            if constexpr (std::is_same<TC, float>::value) {
+                f32x4* dst = reinterpret_cast<f32x4*>(row);
+                if (p.nt_store) __builtin_nontemporal_store(v[j], dst);
+                else *dst = v[j];
+            } else {
+                bf16x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(v[j][r]);
+                bf16x4* dst = reinterpret_cast<bf16x4*>(row);
+                if (p.nt_store) __builtin_nontemporal_store(o, dst);
+                else *dst = o;
             }
         }
     }
@@ -366,16 +412,11 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
     p.mean = g.ln_mean; p.rstd = g.ln_rstd; p.csum = g.ln_csum;
     p.tiles_m = (int)(g.M / BM);
     p.tiles_n = (int)(g.N / BN);
+    p.group = 4;
     p.nt_store = g.M * g.N * (int64_t)sizeof(TC) > ((int64_t)128 << 20);
     const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n);
-    const bool odd = (g.K / BK) & 1;
-    if (g.ln_mean) {
-        if (odd) gemm_bf16_mfma<WB, EPI, true, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-        else gemm_bf16_mfma<WB, EPI, true, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-    } else {
-        if (odd) gemm_bf16_mfma<WB, EPI, false, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-        else gemm_bf16_mfma<WB, EPI, false, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-    }
+    if (g.ln_mean) gemm_bf16_mfma<WB, EPI, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+    else gemm_bf16_mfma<WB, EPI, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -396,20 +437,26 @@ static int device_cus() {
 }
 
 // Whether the MFMA kernel can take a shape with tiles of 64*wb rows: bf16
-// operands, M and N whole tiles, K a whole number (at least two) of 64-wide
-// steps, 16-byte aligned rows, one operand tile's byte offsets below 2^31
+// operands, M and N whole tiles, K a whole number (at least three) of
+// 64-wide steps, 16-byte aligned rows, one operand tile's byte offsets below 2^31
 // (buffer offsets), and, with the LayerNorm epilogue, the column sums of Bop.
 static bool fits_tile(const GemmArgs& g, int wb) {
     const int64_t tm = 64 * wb;
     if (g.ab_dtype != kBF16) return false;
     if (g.M <= 0 || g.N <= 0 || g.K <= 0) return false;
-    if (g.M % tm || g.N % tm || g.K % BK || g.K < 2 * BK) return false;
+    if (g.M % tm || g.N % tm || g.K % BK || g.K < 3 * BK) return false;
     if (g.lda % 8 || g.ldb % 8 || !aligned16(g.A) || !aligned16(g.B)) return false;
     if (tm * g.lda * 2 >= ((int64_t)1 << 31) || tm * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
     if ((g.M / tm) * (g.N / tm) >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) ||
         g.N >= ((int64_t)1 << 31) || g.K >= ((int64_t)1 << 31))
         return false;
     if (g.ln_mean && !g.ln_csum) return false;
+    // the epilogue moves four consecutive columns per lane: 16-byte (fp32)
+    // or 8-byte (bf16) stores and residual loads, 16-byte column-sum loads
+    const int64_t c_es = g.c_dtype == kF32 ? 4 : 2;
+    if (g.ldc % 4 || (reinterpret_cast<uintptr_t>(g.C) & (4 * c_es - 1))) return false;
+    if (g.R && (g.ldr % 4 || (reinterpret_cast<uintptr_t>(g.R) & 7))) return false;
+    if (g.ln_mean && !aligned16(g.ln_csum)) return false;
     return true;
 }
 
