@@ -109,8 +109,8 @@ SHAPES = [
     (257, 129, 384, 4, "bf16"),
     (300, 256, 512, 2, "bf16"),
     (256, 64, 256, 1, "bf16"),
-    (256, 128, 256, 1, "bf16"),     # 256x256 kernel with the minimum K (four steps)
-    (512, 256, 512, 2, "bf16"),     # one steady-state iteration plus the tail
+    (256, 128, 256, 1, "bf16"),     # GEMM1 K = 128: generic kernel; GEMM2 on 128x128 tiles
+    (512, 256, 512, 2, "bf16"),     # 128x128 tiles, K = 256 and 512
     (512, 384, 1536, 4, "bf16"),
     (512, 256, 1024, 4, "bf16"),
     (768, 512, 768, 3, "bf16"),
@@ -124,6 +124,28 @@ def test_shapes(M, D, F, n, dtype):
     inp = workloads.random_case(M, D, F, seed=M * 7 + D * 3 + F + n, dtype=dtype)
     Y, _, _ = _run(inp, n, dtype)
     assert_close(to_f64(Y), oracle_forward(inp.X, inp.A, inp.B, n), dtype, f"M={M} D={D} F={F} n={n}")
+
+
+# The throughput GEMM streams K through a ring of LDS units with its first
+# step and its last two steps peeled, and needs K >= 3 steps of 64.  These
+# shapes put each tile size on the shortest K runs: 256x256 tiles (GEMM1 with
+# M x F = 4096 x 4096, or GEMM2 with M x D = 4096 x 4096) and 128x128 tiles.
+RING_SHAPES = [
+    # (M, D, F, n): which GEMM hits the ring with how many K steps
+    (4096, 192, 4096, 1),   # GEMM1 256x256, 3 steps (GEMM2 N = 192: generic)
+    (4096, 256, 4096, 2),   # GEMM1 256x256, 4 steps
+    (4096, 320, 4096, 4),   # GEMM1 256x256, 5 steps
+    (4096, 4096, 192, 1),   # GEMM2 256x256, 3 steps (GEMM1 N = 192: generic)
+    (512, 192, 512, 2),     # GEMM1 128x128, 3 steps
+]
+
+
+@pytest.mark.parametrize("M,D,F,n", RING_SHAPES)
+def test_ring_short_k(M, D, F, n):
+    say(f"short K ring M={M} D={D} F={F} n={n}")
+    inp = workloads.random_case(M, D, F, seed=M + 3 * D + 5 * F + n, dtype="bf16")
+    Y, _, _ = _run(inp, n, "bf16")
+    assert_close(to_f64(Y), oracle_forward(inp.X, inp.A, inp.B, n), "bf16", f"M={M} D={D} F={F} n={n}")
 
 
 @pytest.mark.parametrize("M,D,F,n", [(512, 256, 1024, 4), (300, 96, 200, 2)])
