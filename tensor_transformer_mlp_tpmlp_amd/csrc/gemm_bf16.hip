@@ -49,6 +49,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace tpmlp {
@@ -85,6 +86,8 @@ struct FastParams {
     int tiles_m, tiles_n;
     int group;           // tile rows walked together on one XCD
     int nt_store;        // write C with non-temporal stores
+    int splits;          // K is split into `splits` equal ranges (grid = tiles x splits)
+    int64_t c_split_stride;  // elements between the outputs of consecutive K ranges
 };
 
 // s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
@@ -105,20 +108,24 @@ constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
 __device__ __forceinline__ uint32_t lds_key(uint32_t r) { return ((r & 8) >> 2) | ((r & 2) << 1); }
 
 // Blocks reach the 8 XCDs round-robin (block b runs on XCD b % 8).  Give each
-// XCD a contiguous range of tile ids, and walk that range in groups of
-// `group` tile rows, column by column, so that the tiles running at once on
-// an XCD share Aop rows and Bop columns in its L2.  Bijective for any tile
-// count and group.
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int group, int& tm, int& tn) {
-    const int total = tiles_m * tiles_n;
+// XCD a contiguous range of work ids, and walk the tiles of a K range in
+// groups of `group` tile rows, column by column, so that the tiles running at
+// once on an XCD share Aop rows and Bop columns in its L2.  Work id w is tile
+// w % tiles of K range w / tiles.  Bijective for any tile count and group.
+__device__ __forceinline__ void map_work(int bid, int tiles_m, int tiles_n, int splits, int group, int& tm,
+                                         int& tn, int& kz) {
+    const int tiles = tiles_m * tiles_n;
+    const int total = tiles * splits;
     const int xcd = bid & 7, idx = bid >> 3;
     const int per = total >> 3, rem = total & 7;
     const int pid = xcd * per + min(xcd, rem) + idx;
+    kz = pid / tiles;
+    const int tid = pid - kz * tiles;
     const int group_tiles = group * tiles_n;
-    const int g = pid / group_tiles;
+    const int g = tid / group_tiles;
     const int first_m = g * group;
     const int gm = min(tiles_m - first_m, group);
-    const int local = pid - g * group_tiles;
+    const int local = tid - g * group_tiles;
     tm = first_m + local % gm;
     tn = local / gm;
 }
@@ -173,18 +180,20 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, kept in an SGPR
     const int wm = w >> 1, wn = w & 1;
-    int tm, tn;
-    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group, tm, tn);
+    int tm, tn, kz;
+    map_work(blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.group, tm, tn, kz);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
+    const int kc = p.K / p.splits;      // this block's K range: [kz kc, (kz+1) kc)
+    const int64_t k0 = (int64_t)kz * kc;
 
-    // Buffer resources over this tile's rows of each operand.
-    const uint32_t a_bytes = (uint32_t)(BM * p.lda * 2);
-    const uint32_t b_bytes = (uint32_t)(BN * p.ldb * 2);
+    // Buffer resources over this tile's rows of each operand, from its K range on.
+    const uint32_t a_bytes = (uint32_t)(BM * p.lda * 2 - k0 * 2);
+    const uint32_t b_bytes = (uint32_t)(BN * p.ldb * 2 - k0 * 2);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(p.A + m0 * p.lda), (short)0, (int)a_bytes, 0x00020000);
+        const_cast<bf16*>(p.A + m0 * p.lda + k0), (short)0, (int)a_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(p.B + n0 * p.ldb), (short)0, (int)b_bytes, 0x00020000);
+        const_cast<bf16*>(p.B + n0 * p.ldb + k0), (short)0, (int)b_bytes, 0x00020000);
 
     // Wave w fills rows [w BM/4, (w+1) BM/4) of a unit with LPU loads of 8
     // rows (1 KiB); in load q, lane L fills row w BM/4 + 8 q + L/8 at physical
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 
     bf16x8 fa0[NB], fb0[NB], fa1[NB], fb1[NB];
-    const int nk = p.K / BK;
+    const int nk = kc / BK;
     __builtin_assume(nk >= 3);
 
     // Per sub-step: NM MFMAs; the NR fragment reads of the next sub-step go
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // n .. n+3 with n = ... + 4 (l >> 4) of block j.  A whole row block is
     // transformed before it is stored, which gives the scheduler NB * 4
     // independent GeLU chains to interleave.
-    TC* __restrict__ C = static_cast<TC*>(p.C);
+    TC* __restrict__ C = static_cast<TC*>(p.C) + kz * p.c_split_stride;
     const int64_t n_base = n0 + wn * 16 * NB + 4 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -401,7 +410,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
 }
 
 template <int WB, int EPI, typename TC>
-hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
+hipError_t launch_typed(const GemmArgs& g, int splits, hipStream_t stream) {
     constexpr int BM = Tile<WB>::M, BN = Tile<WB>::M;
     FastParams p;
     p.A = static_cast<const bf16*>(g.A); p.lda = g.lda;
@@ -414,7 +423,9 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
     p.tiles_n = (int)(g.N / BN);
     p.group = 4;
     p.nt_store = g.M * g.N * (int64_t)sizeof(TC) > ((int64_t)128 << 20);
-    const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n);
+    p.splits = splits;
+    p.c_split_stride = splits > 1 ? g.M * g.N : 0;
+    const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n * splits);
     if (g.ln_mean) gemm_bf16_mfma<WB, EPI, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
     else gemm_bf16_mfma<WB, EPI, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
     return hipGetLastError();
@@ -471,14 +482,97 @@ static int choose_wb(const GemmArgs& g) {
 
 GemmPath choose_gemm_path(const GemmArgs& g) { return choose_wb(g) ? kPathFastBf16 : kPathGeneric; }
 
+// Split-K plan: a GEMM with a plain store epilogue and no LayerNorm whose
+// output tiles fill at most a quarter of the workgroup slots (two per CU at
+// 128x128, one at 256x256) runs its K loop as S equal ranges, S the largest
+// power of two (at most 8) that keeps tiles x S within the slots and each
+// range a whole number (at least three) of 64-wide steps.  Each range
+// writes fp32 partial sums; split_reduce_kernel adds them in range order.
+static int split_count(const GemmArgs& g, int wb) {
+    if (g.epi != kEpiStore || g.ln_mean) return 1;
+    const int64_t tm = 64 * wb;
+    const int64_t tiles = (g.M / tm) * (g.N / tm);
+    const int64_t slots = (int64_t)device_cus() * (wb == 2 ? 2 : 1);
+    if (tiles * 4 > slots) return 1;
+    int s = 1;
+    while (s < 8 && tiles * s * 2 <= slots && g.K % (2 * s * BK) == 0 && g.K / (2 * s) >= 3 * BK) s *= 2;
+    return s;
+}
+
+size_t gemm_split_bytes(const GemmArgs& g) {
+    const int wb = choose_wb(g);
+    if (!wb) return 0;
+    const int s = split_count(g, wb);
+    return s > 1 ? (size_t)s * (size_t)g.M * (size_t)g.N * sizeof(float) : 0;
+}
+
+namespace {
+
+// C[m][n] = sum over r = 0..S-1, in that order, of part[r][m][n] (+ R[m][n]),
+// rounded to C's dtype: the epilogue of a split GEMM.  Four columns per
+// thread (N is a multiple of 128).
+template <typename TC>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int S, int64_t M,
+                                                          int64_t N, const bf16* __restrict__ R, int64_t ldr,
+                                                          TC* __restrict__ C, int64_t ldc) {
+    const int64_t quads = M * N / 4;
+    const int64_t slice = M * N;
+    for (int64_t qi = (int64_t)blockIdx.x * 256 + threadIdx.x; qi < quads; qi += (int64_t)gridDim.x * 256) {
+        const int64_t e = qi * 4;
+        const int64_t m = e / N, n = e - m * N;
+        f32x4 v = *reinterpret_cast<const f32x4*>(part + e);
+        for (int r = 1; r < S; ++r) v += *reinterpret_cast<const f32x4*>(part + r * slice + e);
+        if (R) {
+            const bf16x4 rv = *reinterpret_cast<const bf16x4*>(R + m * ldr + n);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] += static_cast<float>(rv[k]);
+        }
+        if constexpr (std::is_same<TC, float>::value) {
+            *reinterpret_cast<f32x4*>(C + m * ldc + n) = v;
+        } else {
+            bf16x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = static_cast<bf16>(v[k]);
+            *reinterpret_cast<bf16x4*>(C + m * ldc + n) = o;
+        }
+    }
+}
+
+}  // namespace
+
 template <int WB>
 static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
-    if (g.epi == kEpiGelu) return launch_typed<WB, kEpiGelu, bf16>(g, stream);
-    return g.c_dtype == kF32 ? launch_typed<WB, kEpiStore, float>(g, stream)
-                             : launch_typed<WB, kEpiStore, bf16>(g, stream);
+    if (g.epi == kEpiGelu) return launch_typed<WB, kEpiGelu, bf16>(g, 1, stream);
+    const int s = split_count(g, WB);
+    if (s > 1) {
+        // K ranges write fp32 partials, then one pass sums them
+        GemmArgs gp = g;
+        gp.C = g.split_ws;
+        gp.ldc = g.N;
+        gp.c_dtype = kF32;
+        gp.R = nullptr;
+        hipError_t e = launch_typed<WB, kEpiStore, float>(gp, s, stream);
+        if (e != hipSuccess) return e;
+        const int64_t quads = g.M * g.N / 4;
+        const unsigned blocks = (unsigned)std::min<int64_t>((quads + 255) / 256, 8 * (int64_t)device_cus());
+        const float* part = static_cast<const float*>(g.split_ws);
+        const bf16* R = static_cast<const bf16*>(g.R);
+        if (g.c_dtype == kF32)
+            split_reduce_kernel<float><<<dim3(blocks), dim3(256), 0, stream>>>(part, s, g.M, g.N, R, g.ldr,
+                                                                            static_cast<float*>(g.C), g.ldc);
+        else
+            split_reduce_kernel<bf16><<<dim3(blocks), dim3(256), 0, stream>>>(part, s, g.M, g.N, R, g.ldr,
+                                                                           static_cast<bf16*>(g.C), g.ldc);
+        return hipGetLastError();
+    }
+    return g.c_dtype == kF32 ? launch_typed<WB, kEpiStore, float>(g, 1, stream)
+                             : launch_typed<WB, kEpiStore, bf16>(g, 1, stream);
 }
 
 hipError_t launch_gemm_bf16_fast(const GemmArgs& g, hipStream_t stream) {
+    if (gemm_split_bytes(g) > 0 && (!g.split_ws || g.split_ws_bytes < gemm_split_bytes(g) ||
+                                    (reinterpret_cast<uintptr_t>(g.split_ws) & 15)))
+        return hipErrorInvalidValue;
     return choose_wb(g) == 2 ? launch_wb<2>(g, stream) : launch_wb<4>(g, stream);
 }
 

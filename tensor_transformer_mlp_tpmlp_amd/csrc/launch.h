@@ -33,7 +33,15 @@ struct GemmArgs {
     const float* ln_csum = nullptr;  // column sums of Bop over K (LayerNorm epilogue form)
     int epi = kEpiStore;
     int ab_dtype = kBF16;
+    // Split-K scratch (fp32 partial sums); gemm_split_bytes(g) bytes.  Only
+    // a GEMM that would leave most of the GPU idle (few output tiles, long
+    // K, a plain store epilogue) is split; the others ignore it.
+    void* split_ws = nullptr;
+    size_t split_ws_bytes = 0;
 };
+
+// Bytes of split-K scratch launch_gemm will use for g (0: not split).
+size_t gemm_split_bytes(const GemmArgs& g);
 
 // Which kernel family a GEMM goes to.
 enum GemmPath { kPathFastBf16 = 0, kPathGeneric = 1 };

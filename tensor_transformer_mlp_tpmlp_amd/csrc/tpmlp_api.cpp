@@ -45,11 +45,26 @@ tpmlp_status check_shard_args(int64_t D, int64_t F, int n, int dtype) {
     return TPMLP_OK;
 }
 
+// GEMM2's shape as the forward launches it, with stand-in (aligned) operand
+// pointers: what the workspace size depends on.
+GemmArgs gemm2_shape(const tpmlp_shards* s, int64_t M, int64_t nh) {
+    GemmArgs g;
+    char* const fake = reinterpret_cast<char*>((uintptr_t)256);
+    g.A = fake; g.lda = nh;
+    g.B = fake; g.ldb = s->F;
+    g.M = M; g.N = s->D; g.K = nh;
+    g.C = fake; g.ldc = s->D; g.c_dtype = s->dtype;
+    g.epi = kEpiStore;
+    g.ab_dtype = s->dtype;
+    return g;
+}
+
 // Workspace layout for a forward over M rows with N_h intermediate columns:
-//   [H: M x N_h, weights' dtype][mean: M fp32][rstd: M fp32], each segment
-//   256-byte aligned.
+//   [H: M x N_h, weights' dtype][mean: M fp32][rstd: M fp32]
+//   [GEMM2 split-K partials: S x M x D fp32, when GEMM2 is split],
+// each segment 256-byte aligned.
 struct WsLayout {
-    size_t h_off, mean_off, rstd_off, total;
+    size_t h_off, mean_off, rstd_off, split_off, split_bytes, total;
 };
 
 WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard) {
@@ -64,6 +79,9 @@ WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard
         L.rstd_off = off;
         off += round_up((size_t)M * 4);
     }
+    L.split_off = off;
+    L.split_bytes = M > 0 ? gemm_split_bytes(gemm2_shape(s, M, nh)) : 0;
+    off += round_up(L.split_bytes);
     L.total = off;
     return L;
 }
@@ -266,6 +284,8 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
         g2.R = o.residual; g2.ldr = D;
         g2.epi = kEpiStore;
         g2.ab_dtype = s->dtype;
+        g2.split_ws = wsb + L.split_off;
+        g2.split_ws_bytes = L.split_bytes;
         e = launch_gemm(g2, hs);
     }
     if (e == hipSuccess) e = mark(3);
