@@ -5,6 +5,8 @@ from .tpmlp_oracle import (  # noqa: F401
     LN_EPS,
     SQRT_2_OVER_PI,
     gelu,
+    gelu_grad,
+    gelu_grad_scalar,
     gelu_scalar,
     layer_norm,
     layer_norm_loops,
@@ -12,5 +14,8 @@ from .tpmlp_oracle import (  # noqa: F401
     shard_mlp,
     shard_outputs,
     tp_mlp,
+    tp_mlp_backward,
+    tp_mlp_backward_full,
+    tp_mlp_backward_loops,
     tp_mlp_loops,
 )

@@ -17,6 +17,13 @@ FFN half of a block, out = x + TP-MLP(LayerNorm(x)), follows the code
 walkthrough of "LLM Lab Notes 06: Building a Megatron-Style Transformer
 Block from Scratch", section 2, markers 5 to 7.
 
+The backward pass of the same MLP (the gradients of a loss L given
+dY = dL/dY) follows from the chain rule applied to the forward as defined
+above; the pages print no backward formulas, but "LLM Lab Notes 06"
+(section 2, marker 1, and the ledger of section 3) state that backward
+all-reduces the gradient at the same point the forward all-reduced, which
+here is the sum over shards of the input gradient.
+
 Everything is evaluated in float64 with plain numpy matmuls, in the order the
 pages state the steps; there is no blocking, fusion or reordering.  A second,
 pure-Python implementation (``*_loops``) exists for tiny inputs so that the
@@ -144,6 +151,58 @@ def post_ln_ffn(x, shards, eps: float = LN_EPS) -> np.ndarray:
     return x + tp_mlp(layer_norm(x, eps), shards)
 
 
+def gelu_grad(x) -> np.ndarray:
+    """Derivative of the tanh-GeLU of "Tensor-Parallel MLP (Megatron)",
+    section "GeLU", in float64.
+
+    With u = sqrt(2/pi) (x + 0.044715 x^3) and g(x) = x (1 + tanh u) / 2,
+    the product and chain rules give
+    g'(x) = (1 + tanh u) / 2 + x (1 - tanh^2 u) sqrt(2/pi) (1 + 3 * 0.044715 x^2) / 2.
+    """
+    x = _f64(x)
+    with np.errstate(over="ignore", invalid="ignore"):
+        u = SQRT_2_OVER_PI * (x + GELU_CUBIC * (x * x * x))
+        t = np.tanh(u)
+        du = SQRT_2_OVER_PI * (1.0 + 3.0 * GELU_CUBIC * (x * x))
+        return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * du
+
+
+def tp_mlp_backward(X, shards: Sequence[Tuple[np.ndarray, np.ndarray]], dY):
+    """Gradients of the TP-MLP given dY = dL/dY, shard by shard.
+
+    Forward ("Tensor-Parallel MLP (Megatron)", "The split"): S_i = X A_i,
+    H_i = GeLU(S_i), Y = sum_i H_i B_i.  The chain rule gives, for each i,
+        dB_i = H_i^T dY,   dS_i = (dY B_i^T) * GeLU'(S_i),   dA_i = X^T dS_i,
+    and the input gradient dX = sum_i dS_i A_i^T, summed over shards in
+    ascending i: the backward all-reduce of "LLM Lab Notes 06", section 2,
+    marker 1 (its autograd function all-reduces the incoming gradient) and
+    the backward row of the ledger in section 3.
+    Returns (dX, [dA_i], [dB_i]).
+    """
+    X = _f64(X)
+    dY = _f64(dY)
+    dX = np.zeros_like(X)
+    dA_list, dB_list = [], []
+    for A_i, B_i in shards:
+        A_i = _f64(A_i)
+        B_i = _f64(B_i)
+        S_i = X @ A_i
+        H_i = gelu(S_i)
+        dB_list.append(H_i.T @ dY)
+        dS_i = (dY @ B_i.T) * gelu_grad(S_i)
+        dA_list.append(X.T @ dS_i)
+        dX = dX + dS_i @ A_i.T
+    return dX, dA_list, dB_list
+
+
+def tp_mlp_backward_full(X, A, B, n: int, dY):
+    """tp_mlp_backward over shard_mlp(A, B, n), with the per-shard weight
+    gradients placed back where their shards came from: dA (D x F) has dA_i
+    in columns iF/n .. (i+1)F/n - 1, dB (F x D) has dB_i in those rows."""
+    dX, dA_list, dB_list = tp_mlp_backward(X, shard_mlp(A, B, n), dY)
+    return dX, np.concatenate(dA_list, axis=1), np.concatenate(dB_list, axis=0)
+
+
 # --------------------------------------------------------------------------
 # pure-Python oracle (no numpy arithmetic), for tiny inputs only
 # --------------------------------------------------------------------------
@@ -213,3 +272,46 @@ def layer_norm_loops(x, eps: float = LN_EPS):
         inv = 1.0 / math.sqrt(var + eps)
         out.append([(v - mu) * inv for v in row])
     return out
+
+
+def gelu_grad_scalar(x: float) -> float:
+    """Scalar derivative of the tanh-GeLU (same formula as gelu_grad)."""
+    x = float(x)
+    u = SQRT_2_OVER_PI * (x + GELU_CUBIC * x * x * x)
+    t = math.tanh(u)
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * SQRT_2_OVER_PI * (1.0 + 3.0 * GELU_CUBIC * x * x)
+
+
+def tp_mlp_backward_loops(X, A, B, n: int, dY):
+    """Pure-Python version of tp_mlp_backward_full on nested lists: the same
+    chain-rule steps, entry by entry.  Returns (dX, dA, dB) as nested lists."""
+    X = [[float(v) for v in row] for row in X]
+    A = [[float(v) for v in row] for row in A]
+    B = [[float(v) for v in row] for row in B]
+    dY = [[float(v) for v in row] for row in dY]
+    D, F = len(A), len(A[0])
+    M = len(X)
+    if F % n:
+        raise ValueError("F must be divisible by n")
+    w = F // n
+    dX = [[0.0] * D for _ in range(M)]
+    dA = [[0.0] * F for _ in range(D)]
+    dB = [[0.0] * D for _ in range(F)]
+    for i in range(n):
+        cols = range(i * w, (i + 1) * w)
+        for f in cols:
+            # column f of S = X A, of H = GeLU(S) and of dS
+            s_col = [sum(X[m][d] * A[d][f] for d in range(D)) for m in range(M)]
+            h_col = [gelu_scalar(v) for v in s_col]
+            dh_col = [sum(dY[m][d] * B[f][d] for d in range(D)) for m in range(M)]
+            ds_col = [dh_col[m] * gelu_grad_scalar(s_col[m]) for m in range(M)]
+            for d in range(D):
+                dB[f][d] = sum(h_col[m] * dY[m][d] for m in range(M))
+                dA[d][f] = sum(X[m][d] * ds_col[m] for m in range(M))
+        for m in range(M):
+            for d in range(D):
+                dX[m][d] += sum(
+                    sum(dY[m][e] * B[f][e] for e in range(D))
+                    * gelu_grad_scalar(sum(X[m][k] * A[k][f] for k in range(D))) * A[d][f]
+                    for f in cols)
+    return dX, dA, dB
