@@ -201,6 +201,41 @@ void tpmlp_opts_init(tpmlp_opts* o);
 tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, void* Y,
                               const tpmlp_opts* opts, void* stream);
 
+/*
+ * Bytes of device workspace tpmlp_backward needs for M rows: the weights
+ * unpacked to A (D x F) and B (F x D), three M x F intermediates (S = X A,
+ * H = GeLU(S) and dS), transposed copies of X and dY (D x M each), all in
+ * the weights' dtype, plus the split-K scratch of its GEMMs.  Returns 0 for
+ * invalid arguments.
+ */
+size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M);
+
+/*
+ * tpmlp_backward -- gradients of the TP-MLP for a loss L, given dY = dL/dY.
+ * With S_i = X A_i and H_i = GeLU_tanh(S_i) ("Tensor-Parallel MLP
+ * (Megatron)", section "The split", bullets 1 and 2), the chain rule gives
+ *   dB_i = H_i^T dY,  dS_i = (dY B_i^T) * GeLU'(S_i),  dA_i = X^T dS_i,
+ *   dX = sum_i dS_i A_i^T,
+ * the last sum being the backward all-reduce of "LLM Lab Notes 06", section
+ * 2, marker 1 and the ledger of section 3 (formed here in one fp32
+ * accumulator, like the forward's).  S is recomputed from X; S, H and dS are
+ * held in the weights' dtype between the GEMMs.
+ *   X, dY  device, M x D row-major, the descriptor's dtype.
+ *   M      rows; 0 gives dX nothing to write and zero dA, dB.
+ *   s      descriptor from tpmlp_shard (its packed weights are read only).
+ *   dX     device, M x D, the descriptor's dtype.
+ *   dA     device, D x F: dA_i in columns iF/n .. (i+1)F/n - 1 (A's layout).
+ *   dB     device, F x D: dB_i in rows iF/n .. (i+1)F/n - 1 (B's layout).
+ *   workspace  device, at least tpmlp_backward_workspace_bytes(s, M) bytes,
+ *          16-byte aligned, caller-owned; contents are scratch.
+ * Outputs must not overlap each other, the inputs or the workspace.
+ * Errors: TPMLP_ERR_NULL, TPMLP_ERR_SHAPE (M < 0 or too large),
+ * TPMLP_ERR_ALIGN, TPMLP_ERR_WORKSPACE, TPMLP_ERR_HIP; all but the last are
+ * returned before any HIP call.
+ */
+tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpmlp_shards* s, void* dX, void* dA,
+                            void* dB, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

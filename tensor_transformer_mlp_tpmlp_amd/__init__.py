@@ -16,4 +16,5 @@ from .tpmlp import (  # noqa: F401
     lib,
     shard_mlp,
     tp_mlp,
+    tp_mlp_backward,
 )

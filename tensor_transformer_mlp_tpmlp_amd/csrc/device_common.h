@@ -33,6 +33,19 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
+// d/dx GeLU_tanh(x), for the backward pass.  With s = (1 + tanh u)/2 =
+// 1/(1 + exp(-2u)) and 1 - tanh^2 u = 4 s (1 - s), the product and chain
+// rules give s (1 + q (1 - s)), q = 2 sqrt(2/pi) x (1 + 3 * 0.044715 x^2).
+// exp(-2u) overflows to +inf for very negative x; then s = 0 and the result
+// is 0 (without the select, 0 * x^3 could become NaN for huge |x|).
+__device__ __forceinline__ float gelu_tanh_grad(float x) {
+    const float z = x * __builtin_fmaf(x * x, kGeluK1, kGeluK0);
+    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
+    const float q = (2.0f * kGeluC) * x * __builtin_fmaf((3.0f * kGeluA) * x, x, 1.0f);
+    const float r = s * __builtin_fmaf(q, 1.0f - s, 1.0f);
+    return s == 0.0f ? 0.0f : r;
+}
+
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
 

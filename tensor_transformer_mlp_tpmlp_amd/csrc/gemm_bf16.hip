@@ -83,6 +83,8 @@ struct FastParams {
     const float* mean;   // LayerNorm: per-row mean and 1/sqrt(var+eps)
     const float* rstd;
     const float* csum;   // LayerNorm: per-column sums of Bop (= column sums of A)
+    const bf16* aux;     // kEpiGeluGrad: pre-activation, M x N
+    int64_t ldaux;
     int tiles_m, tiles_n;
     int group;           // tile rows walked together on one XCD
     int nt_store;        // write C with non-temporal stores
@@ -376,6 +378,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
         }
         if constexpr (EPI == kEpiGelu) {
             gelu_tanh_staged(v);
+        } else if constexpr (EPI == kEpiGeluGrad) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const bf16x4 sv = *reinterpret_cast<const bf16x4*>(p.aux + m * p.ldaux + n_base + j * 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[j][r] *= gelu_tanh_grad(static_cast<float>(sv[r]));
+            }
         } else {
             if (p.R) {
 #pragma unroll
@@ -419,6 +428,7 @@ hipError_t launch_typed(const GemmArgs& g, int splits, hipStream_t stream) {
     p.C = g.C; p.ldc = g.ldc;
     p.R = static_cast<const bf16*>(g.R); p.ldr = g.ldr;
     p.mean = g.ln_mean; p.rstd = g.ln_rstd; p.csum = g.ln_csum;
+    p.aux = static_cast<const bf16*>(g.aux); p.ldaux = g.ldaux;
     p.tiles_m = (int)(g.M / BM);
     p.tiles_n = (int)(g.N / BN);
     p.group = 4;
@@ -468,6 +478,9 @@ static bool fits_tile(const GemmArgs& g, int wb) {
     if (g.ldc % 4 || (reinterpret_cast<uintptr_t>(g.C) & (4 * c_es - 1))) return false;
     if (g.R && (g.ldr % 4 || (reinterpret_cast<uintptr_t>(g.R) & 7))) return false;
     if (g.ln_mean && !aligned16(g.ln_csum)) return false;
+    if (g.epi == kEpiGeluGrad && (!g.aux || g.ldaux % 4 || (reinterpret_cast<uintptr_t>(g.aux) & 7) ||
+                                  g.c_dtype != kBF16))
+        return false;
     return true;
 }
 
@@ -543,6 +556,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 template <int WB>
 static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
     if (g.epi == kEpiGelu) return launch_typed<WB, kEpiGelu, bf16>(g, 1, stream);
+    if (g.epi == kEpiGeluGrad) return launch_typed<WB, kEpiGeluGrad, bf16>(g, 1, stream);
     const int s = split_count(g, WB);
     if (s > 1) {
         // K ranges write fp32 partials, then one pass sums them

@@ -32,6 +32,8 @@ struct GenericParams {
     int64_t ldr;
     const float* mean;
     const float* rstd;
+    const void* aux;     // kEpiGeluGrad: pre-activation, operand dtype
+    int64_t ldaux;
     int64_t tiles_n;
 };
 
@@ -107,6 +109,8 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GenericParams p) {
             float v = acc[r];
             if constexpr (EPI == kEpiGelu) {
                 v = gelu_tanh(v);
+            } else if constexpr (EPI == kEpiGeluGrad) {
+                v *= gelu_tanh_grad(to_f32(static_cast<const T*>(p.aux)[m * p.ldaux + n]));
             } else {
                 if (R) v += to_f32(R[m * p.ldr + n]);
             }
@@ -122,6 +126,7 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
     p.M = g.M; p.N = g.N; p.K = g.K;
     p.C = g.C; p.ldc = g.ldc; p.R = g.R; p.ldr = g.ldr;
     p.mean = g.ln_mean; p.rstd = g.ln_rstd;
+    p.aux = g.aux; p.ldaux = g.ldaux;
     p.tiles_n = (g.N + GT - 1) / GT;
     const int64_t tiles = ((g.M + GT - 1) / GT) * p.tiles_n;
     if (g.ln_mean)
@@ -133,17 +138,17 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
 
 }  // namespace
 
+template <typename T, typename TC>
+static hipError_t launch_epi(const GemmArgs& g, hipStream_t stream) {
+    if (g.epi == kEpiGelu) return launch_typed<T, TC, kEpiGelu>(g, stream);
+    if (g.epi == kEpiGeluGrad) return launch_typed<T, TC, kEpiGeluGrad>(g, stream);
+    return launch_typed<T, TC, kEpiStore>(g, stream);
+}
+
 hipError_t launch_gemm_generic(const GemmArgs& g, hipStream_t stream) {
-    if (g.ab_dtype == kF32) {
-        // fp32 weights produce fp32 results only
-        return g.epi == kEpiGelu ? launch_typed<float, float, kEpiGelu>(g, stream)
-                                 : launch_typed<float, float, kEpiStore>(g, stream);
-    }
-    if (g.c_dtype == kF32)
-        return g.epi == kEpiGelu ? launch_typed<bf16, float, kEpiGelu>(g, stream)
-                                 : launch_typed<bf16, float, kEpiStore>(g, stream);
-    return g.epi == kEpiGelu ? launch_typed<bf16, bf16, kEpiGelu>(g, stream)
-                             : launch_typed<bf16, bf16, kEpiStore>(g, stream);
+    if (g.ab_dtype == kF32) return launch_epi<float, float>(g, stream);  // fp32 weights: fp32 results
+    if (g.c_dtype == kF32) return launch_epi<bf16, float>(g, stream);
+    return launch_epi<bf16, bf16>(g, stream);
 }
 
 }  // namespace tpmlp

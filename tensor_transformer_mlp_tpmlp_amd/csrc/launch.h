@@ -11,6 +11,7 @@ constexpr int kBF16 = 1;
 
 constexpr int kEpiGelu = 0;   // C = GeLU_tanh(acc), rounded to C's dtype
 constexpr int kEpiStore = 1;  // C = acc (+ R), rounded to C's dtype
+constexpr int kEpiGeluGrad = 2;  // C = acc * GeLU_tanh'(aux), aux M x N in ab_dtype (backward)
 
 // C[m][n] = epi( sum_k a(m,k) * Bop[n][k] ), m < M, n < N, k < K, where
 // a(m,k) = Aop[m][k], or (Aop[m][k] - ln_mean[m]) * ln_rstd[m] when ln_mean
@@ -33,6 +34,8 @@ struct GemmArgs {
     const float* ln_csum = nullptr;  // column sums of Bop over K (LayerNorm epilogue form)
     int epi = kEpiStore;
     int ab_dtype = kBF16;
+    const void* aux = nullptr;  // kEpiGeluGrad: the pre-activation, M x N (ldaux)
+    int64_t ldaux = 0;
     // Split-K scratch (fp32 partial sums); gemm_split_bytes(g) bytes.  Only
     // a GEMM that would leave most of the GPU idle (few output tiles, long
     // K, a plain store epilogue) is split; the others ignore it.

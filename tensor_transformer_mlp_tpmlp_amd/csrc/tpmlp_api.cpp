@@ -86,6 +86,56 @@ WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard
     return L;
 }
 
+// GEMM shapes of the backward (stand-in aligned pointers), for sizing the
+// split-K scratch they share.
+GemmArgs bwd_shape(int64_t M, int64_t N, int64_t K, int dtype) {
+    GemmArgs g;
+    char* const fake = reinterpret_cast<char*>((uintptr_t)256);
+    g.A = fake; g.lda = K;
+    g.B = fake; g.ldb = K;
+    g.M = M; g.N = N; g.K = K;
+    g.C = fake; g.ldc = N; g.c_dtype = dtype;
+    g.epi = kEpiStore;
+    g.ab_dtype = dtype;
+    return g;
+}
+
+// Backward workspace, each segment 256-byte aligned:
+//   A (D x F) and B (F x D) unpacked from the shard buffer,
+//   S = X A (M x F), later H^T (F x M);  H = GeLU(S) (M x F), later dS^T;
+//   dS (M x F);  X^T (D x M);  dY^T (D x M);  split-K scratch.
+struct BwdLayout {
+    size_t a, b, s_ht, h_dst, ds, xt, dyt, split, split_bytes, total;
+};
+
+BwdLayout bwd_layout(const tpmlp_shards* s, int64_t M) {
+    const size_t es = elem_size(s->dtype);
+    const size_t D = (size_t)s->D, F = (size_t)s->F, m = (size_t)M;
+    BwdLayout L;
+    size_t off = 0;
+    L.a = off; off += round_up(D * F * es);
+    L.b = off; off += round_up(F * D * es);
+    L.s_ht = off; off += round_up(m * F * es);
+    L.h_dst = off; off += round_up(m * F * es);
+    L.ds = off; off += round_up(m * F * es);
+    L.xt = off; off += round_up(D * m * es);
+    L.dyt = off; off += round_up(D * m * es);
+    size_t sb = 0;
+    if (M > 0) {
+        const int dt = s->dtype;
+        const size_t cand[4] = {gemm_split_bytes(bwd_shape(M, s->F, s->D, dt)),   // S = X A
+                                gemm_split_bytes(bwd_shape(M, s->D, s->F, dt)),   // dX = dS A^T
+                                gemm_split_bytes(bwd_shape(s->D, s->F, M, dt)),   // dA = X^T dS
+                                gemm_split_bytes(bwd_shape(s->F, s->D, M, dt))};  // dB = H^T dY
+        for (size_t c : cand) sb = c > sb ? c : sb;
+    }
+    L.split = off;
+    L.split_bytes = sb;
+    off += round_up(sb);
+    L.total = off;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,6 +344,81 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
 
 tpmlp_status tpmlp_forward(const void* X, int64_t M, const tpmlp_shards* s, void* Y, void* stream) {
     return tpmlp_forward_ex(X, M, s, Y, nullptr, stream);
+}
+
+size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M) {
+    if (!s || M < 0 || M > kMaxDim) return 0;
+    return bwd_layout(s, M).total;
+}
+
+tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpmlp_shards* s, void* dX, void* dA,
+                            void* dB, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!s) return TPMLP_ERR_NULL;
+    if (M < 0 || M > kMaxDim) return TPMLP_ERR_SHAPE;
+    if (!dA || !dB || (M > 0 && (!X || !dY || !dX))) return TPMLP_ERR_NULL;
+    if (!aligned16(dA) || !aligned16(dB) || (M > 0 && (!aligned16(X) || !aligned16(dY) || !aligned16(dX))))
+        return TPMLP_ERR_ALIGN;
+    const BwdLayout L = bwd_layout(s, M);
+    if (!workspace || workspace_bytes < L.total) return TPMLP_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TPMLP_ERR_ALIGN;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int dt = s->dtype;
+    const int eb = (int)elem_size(dt);
+    const int64_t D = s->D, F = s->F;
+    const char* at = static_cast<const char*>(s->packed);                     // A^T: F x D
+    const char* bt = at + round_up((size_t)D * (size_t)F * eb);              // B^T: D x F
+    char* w = static_cast<char*>(workspace);
+    auto gemm = [&](const void* A, int64_t lda, const void* B, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                    void* C, int64_t ldc, int epi, const void* aux) {
+        GemmArgs g;
+        g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
+        g.M = m; g.N = n; g.K = k;
+        g.C = C; g.ldc = ldc; g.c_dtype = dt;
+        g.epi = epi; g.ab_dtype = dt;
+        g.aux = aux; g.ldaux = n;
+        g.split_ws = w + L.split; g.split_ws_bytes = L.split_bytes;
+        return launch_gemm(g, hs);
+    };
+
+    if (M == 0) {
+        // an empty batch contributes zero weight gradients: K = 0 GEMMs
+        // read no operand and write zeros
+        GemmArgs za = bwd_shape(D, F, 0, dt);
+        za.A = dA; za.B = dA; za.C = dA;
+        GemmArgs zb = bwd_shape(F, D, 0, dt);
+        zb.A = dB; zb.B = dB; zb.C = dB;
+        hipError_t e = launch_gemm_generic(za, hs);
+        if (e == hipSuccess) e = launch_gemm_generic(zb, hs);
+        return from_hip(e);
+    }
+
+    void* Aw = w + L.a;        // A: D x F
+    void* Bw = w + L.b;        // B: F x D
+    void* S = w + L.s_ht;      // S: M x F, later H^T: F x M
+    void* H = w + L.h_dst;     // H: M x F, later dS^T: F x M
+    void* dS = w + L.ds;       // dS: M x F
+    void* Xt = w + L.xt;       // X^T: D x M
+    void* dYt = w + L.dyt;     // dY^T: D x M
+
+    // The weights in their own layouts ("The split": A is D x F, B is F x D).
+    hipError_t e = launch_transpose(at, D, Aw, F, F, D, eb, hs);
+    if (e == hipSuccess) e = launch_transpose(bt, F, Bw, D, D, F, eb, hs);
+    // S = X A for all shards at once; H = GeLU(S)
+    if (e == hipSuccess) e = gemm(X, D, at, D, M, F, D, S, F, kEpiStore, nullptr);
+    if (e == hipSuccess) e = launch_gelu(S, H, M * F, dt, hs);
+    // dS = (dY B^T) * GeLU'(S): the gradient at every shard's GeLU input
+    if (e == hipSuccess) e = gemm(dY, D, Bw, D, M, F, D, dS, F, kEpiGeluGrad, S);
+    // dX = sum_i dS_i A_i^T: the K loop over F sums the shards in registers
+    if (e == hipSuccess) e = gemm(dS, F, Aw, F, M, D, F, dX, D, kEpiStore, nullptr);
+    // dA = X^T dS and dB = H^T dY: K = M, from transposed copies
+    if (e == hipSuccess) e = launch_transpose(H, F, S, M, M, F, eb, hs);      // H^T into S's space
+    if (e == hipSuccess) e = launch_transpose(dS, F, H, M, M, F, eb, hs);     // dS^T into H's space
+    if (e == hipSuccess) e = launch_transpose(X, D, Xt, M, M, D, eb, hs);
+    if (e == hipSuccess) e = launch_transpose(dY, D, dYt, M, M, D, eb, hs);
+    if (e == hipSuccess) e = gemm(Xt, M, H, M, D, F, M, dA, F, kEpiStore, nullptr);
+    if (e == hipSuccess) e = gemm(S, M, dYt, M, F, D, M, dB, D, kEpiStore, nullptr);
+    return from_hip(e);
 }
 
 }  // extern "C"

@@ -56,6 +56,8 @@ SIGNATURES = {
     "tpmlp_forward": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp]),
     "tpmlp_opts_init": (None, [ctypes.POINTER(Opts)]),
     "tpmlp_forward_ex": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, ctypes.POINTER(Opts), _c_vp]),
+    "tpmlp_backward_workspace_bytes": (_c_sz, [_c_vp, _c_i64]),
+    "tpmlp_backward": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
 }
 
 _lib = None
@@ -237,3 +239,28 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, eps: flo
                               _dev(out, "out") if M else out.data_ptr(), ctypes.byref(o),
                               _stream(X.device)), "tpmlp_forward_ex")
     return out
+
+
+def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards):
+    """Gradients (dX, dA, dB) of the TP-MLP given dY = dL/dY (tpmlp_backward).
+
+    dA has A's layout (D x F, shard i in its columns), dB has B's (F x D,
+    shard i in its rows); all three in the weights' dtype.
+    """
+    if X.dim() != 2 or X.shape[1] != shards.D:
+        raise ValueError(f"X must be (M, {shards.D})")
+    if X.dtype != shards.dtype or dY.dtype != shards.dtype:
+        raise TypeError("X and dY must have the weights' dtype")
+    if tuple(dY.shape) != tuple(X.shape):
+        raise ValueError("dY must have X's shape")
+    M = X.shape[0]
+    dX = torch.empty_like(X)
+    dA = torch.empty((shards.D, shards.F), dtype=shards.dtype, device=X.device)
+    dB = torch.empty((shards.F, shards.D), dtype=shards.dtype, device=X.device)
+    L = lib()
+    nbytes = L.tpmlp_backward_workspace_bytes(shards.handle, M)
+    ws = shards.workspace(nbytes)
+    _check(L.tpmlp_backward(_dev(X, "X") if M else X.data_ptr(), _dev(dY, "dY") if M else dY.data_ptr(), M,
+                            shards.handle, _dev(dX, "dX") if M else dX.data_ptr(), _dev(dA, "dA"),
+                            _dev(dB, "dB"), ws.data_ptr(), ws.numel(), _stream(X.device)), "tpmlp_backward")
+    return dX, dA, dB

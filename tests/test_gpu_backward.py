@@ -1,0 +1,147 @@
+"""GPU parity of the backward pass (tpmlp_backward) against the fp64 oracle.
+
+Every call goes through the C ABI.  Small and mid sizes are compared on every
+element of dX, dA and dB.  The headline size is compared on samples that are
+exactly the oracle of a sub-problem: rows of dX depend only on the same rows
+of X and dY (the oracle of that sub-batch), and column f of dA / row f of dB
+depend only on column f of A and row f of B (the oracle of the MLP restricted
+to the sampled intermediate columns).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import tensor_transformer_mlp_tpmlp_amd as tp
+from parity_util import assert_close, sample_rows, say, to_dev, to_f64, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tp.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _case(M, D, F, seed, dtype, sdy=1.0):
+    inp = workloads.random_case(M, D, F, seed=seed, dtype=dtype)
+    dY = np.random.default_rng(seed + 1).standard_normal((M, D)).astype(np.float32) * sdy
+    if dtype == "bf16":
+        dY = workloads.round_to_bf16(dY)
+    return inp, dY
+
+
+def _gpu_backward(inp, dY, n, dtype):
+    dt = torch_dtype(dtype)
+    X, A, B, tdY = (to_dev(a, dt) for a in (inp.X, inp.A, inp.B, dY))
+    sh = tp.shard_mlp(A, B, n)
+    dX, dA, dB = tp.tp_mlp_backward(X, tdY, sh)
+    torch.cuda.synchronize()
+    return dX, dA, dB
+
+
+BWD_SHAPES = [
+    # (M, D, F, n, dtype)
+    (1, 2, 4, 2, "f32"),
+    (3, 5, 7, 7, "f32"),
+    (130, 70, 96, 3, "f32"),
+    (64, 64, 256, 4, "bf16"),
+    (257, 129, 384, 4, "bf16"),     # odd sizes: the bounds-checked kernel
+    (512, 256, 1024, 4, "bf16"),    # every GEMM on the 128x128 ring kernel
+    (1024, 512, 2048, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,D,F,n,dtype", BWD_SHAPES)
+def test_backward_shapes(M, D, F, n, dtype):
+    say(f"backward M={M} D={D} F={F} n={n} {dtype}")
+    inp, dY = _case(M, D, F, seed=900 + M + D + F + n, dtype=dtype)
+    dX, dA, dB = _gpu_backward(inp, dY, n, dtype)
+    rX, rA, rB = oracle.tp_mlp_backward_full(inp.X, inp.A, inp.B, n, dY)
+    assert_close(to_f64(dX), rX, dtype, "dX")
+    assert_close(to_f64(dA), rA, dtype, "dA")
+    assert_close(to_f64(dB), rB, dtype, "dB")
+
+
+def test_backward_h1024_full():
+    w = workloads.WORKLOADS["mlp_h1024_bf16"]
+    say(f"backward {w.name}")
+    inp = workloads.make_inputs(w)
+    dY = workloads.round_to_bf16(np.random.default_rng(w.seed + 7).standard_normal((w.M, w.D)).astype(np.float32))
+    dX, dA, dB = _gpu_backward(inp, dY, w.n, "bf16")
+    rX, rA, rB = oracle.tp_mlp_backward_full(inp.X, inp.A, inp.B, w.n, dY)
+    assert_close(to_f64(dX), rX, "bf16", "dX")
+    assert_close(to_f64(dA), rA, "bf16", "dA")
+    assert_close(to_f64(dB), rB, "bf16", "dB")
+
+
+def test_backward_headline_sampled():
+    w = workloads.WORKLOADS["mlp_h4096_bf16"]
+    say(f"backward {w.name} (sampled rows of dX, columns of dA, rows of dB)")
+    inp = workloads.make_inputs(w)
+    dY = workloads.round_to_bf16(np.random.default_rng(w.seed + 7).standard_normal((w.M, w.D)).astype(np.float32))
+    dX, dA, dB = _gpu_backward(inp, dY, w.n, "bf16")
+    assert bool(torch.isfinite(dX).all()) and bool(torch.isfinite(dA).all()) and bool(torch.isfinite(dB).all())
+    rows = sample_rows(w.M, 16, seed=w.seed)
+    rX, _, _ = oracle.tp_mlp_backward_full(inp.X[rows], inp.A, inp.B, w.n, dY[rows])
+    assert_close(to_f64(dX[torch.from_numpy(rows).to(dX.device)]), rX, "bf16", f"dX rows {len(rows)}")
+    cols = sample_rows(w.F, 16, seed=w.seed + 1)
+    _, rA, rB = oracle.tp_mlp_backward_full(inp.X, inp.A[:, cols], inp.B[cols, :], 1, dY)
+    idx = torch.from_numpy(cols).to(dA.device)
+    assert_close(to_f64(dA[:, idx]), rA, "bf16", f"dA columns {len(cols)}")
+    assert_close(to_f64(dB[idx, :]), rB, "bf16", f"dB rows {len(cols)}")
+
+
+def test_backward_empty_batch_gives_zero_weight_grads():
+    say("backward M = 0")
+    inp, dY = _case(4, 64, 128, seed=3, dtype="bf16")
+    A, B = to_dev(inp.A, torch.bfloat16), to_dev(inp.B, torch.bfloat16)
+    sh = tp.shard_mlp(A, B, 2)
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    dX, dA, dB = tp.tp_mlp_backward(X, X.clone(), sh)
+    torch.cuda.synchronize()
+    assert dX.shape == (0, 64)
+    assert float(dA.float().abs().max()) == 0.0 and float(dB.float().abs().max()) == 0.0
+
+
+def test_backward_deterministic():
+    say("backward determinism")
+    inp, dY = _case(512, 256, 1024, seed=5, dtype="bf16")
+    a = _gpu_backward(inp, dY, 4, "bf16")
+    b = _gpu_backward(inp, dY, 4, "bf16")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_errors_with_real_descriptor():
+    say("backward error paths")
+    inp, dY = _case(64, 64, 128, seed=2, dtype="f32")
+    X, A, B, tdY = (to_dev(a, torch.float32) for a in (inp.X, inp.A, inp.B, dY))
+    sh = tp.shard_mlp(A, B, 2)
+    L = tp.lib()
+    dX = torch.empty_like(X)
+    dA = torch.empty(64, 128, device="cuda")
+    dB = torch.empty(128, 64, device="cuda")
+    need = L.tpmlp_backward_workspace_bytes(sh.handle, 64)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    args = (X.data_ptr(), tdY.data_ptr(), 64, sh.handle, dX.data_ptr(), dA.data_ptr(), dB.data_ptr())
+    assert L.tpmlp_backward(*args, ws.data_ptr(), need - 1, None) == 5      # workspace too small
+    assert L.tpmlp_backward(*args, None, need, None) == 5
+    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), -1, sh.handle, dX.data_ptr(), dA.data_ptr(),
+                            dB.data_ptr(), ws.data_ptr(), need, None) == 2
+    assert L.tpmlp_backward(X.data_ptr() + 4, tdY.data_ptr(), 64, sh.handle, dX.data_ptr(), dA.data_ptr(),
+                            dB.data_ptr(), ws.data_ptr(), need, None) == 6
+    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), 64, sh.handle, dX.data_ptr(), None,
+                            dB.data_ptr(), ws.data_ptr(), need, None) == 1
+    assert L.tpmlp_backward(*args, ws.data_ptr(), need, None) == 0
+    torch.cuda.synchronize()
+    rX, rA, rB = oracle.tp_mlp_backward_full(inp.X, inp.A, inp.B, 2, dY)
+    assert_close(to_f64(dX), rX, "f32", "dX")
+    assert_close(to_f64(dA), rA, "f32", "dA")
+    assert_close(to_f64(dB), rB, "f32", "dB")
