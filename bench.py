@@ -229,6 +229,84 @@ def cpu_baseline(w, inp, target_s: float):
                        "independent)") + f", D={w.D}, F={w.F}, n={w.n}; numpy fp64 oracle, {t:.1f} s"}
 
 
+BWD_METRIC = "TP-MLP backward TFLOP/s (8·M·D·F: dX, dA, dB), 1 MI355X"
+
+
+def bench_backward(args, w, inp, X, shards, dtype, dev) -> int:
+    """Times tpmlp_backward: gradients dX, dA, dB for a seeded bf16 dY.
+
+    value = 8·M·D·F / t, the algorithmic FLOP of the four gradient GEMMs;
+    the recomputation of S = X A (another 2·M·D·F) is not counted.  The
+    events bracket the whole pass on the library's stream.
+    """
+    import numpy as np
+    import torch
+
+    import tensor_transformer_mlp_tpmlp_amd as tp
+    import workloads
+
+    if w.layernorm or w.residual:
+        raise SystemExit("the backward covers the TP-MLP without LayerNorm or residual")
+    dYh = np.random.default_rng(w.seed + 7).standard_normal((w.M, w.D)).astype(np.float32)
+    if w.dtype == "bf16":
+        dYh = workloads.round_to_bf16(dYh)
+    dY = torch.from_numpy(dYh).to(dev).to(dtype).contiguous()
+    outs = (torch.empty_like(X), torch.empty((w.D, w.F), dtype=dtype, device=dev),
+            torch.empty((w.F, w.D), dtype=dtype, device=dev))
+
+    def step():
+        tp.tp_mlp_backward(X, dY, shards, out=outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"[bench] backward: {args.steps} timed steps, {ms:.4f} ms/step")
+    flops = 8.0 * w.M * w.D * w.F
+    value = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    out = {
+        "metric": BWD_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "strong", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "M": w.M, "D": w.D, "F": w.F, "n": w.n},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "kernel": "whole backward pass", "achieved": round(value, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(value / peak, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] timing the fp64 oracle backward on the host")
+        cores = len(os.sched_getaffinity(0))
+
+        def run(rows):
+            t = time.perf_counter()
+            oracle.tp_mlp_backward_full(inp.X[:rows], inp.A, inp.B, w.n, dYh[:rows])
+            return time.perf_counter() - t
+
+        run(min(16, w.M))
+        probe = min(64, w.M)
+        t_probe = run(probe)
+        rows = w.M if t_probe * w.M / probe <= args.cpu_seconds else max(probe, int(probe * args.cpu_seconds / t_probe))
+        rows = min(rows, w.M)
+        t_cpu = run(rows)
+        out["cpu_baseline"] = {
+            "value": 8.0 * rows * w.D * w.F / t_cpu / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{'all' if rows == w.M else 'first'} {rows} of {w.M} rows of X and dY, D={w.D}, F={w.F}, "
+                       f"n={w.n}; numpy fp64 oracle backward (S, H, dS, dX, dA, dB), {t_cpu:.1f} s; the weight "
+                       "gradients over a row prefix cost the same per row as over all rows"),
+        }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +320,8 @@ def main() -> int:
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output of this bench")
     ap.add_argument("--profile-command", default="", help="command recorded in the profile summary")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+                    help="time the forward (default, the headline metric) or the backward pass")
     args = ap.parse_args()
 
     if args.summarize_profiles:
@@ -280,6 +360,8 @@ def main() -> int:
     Y = torch.empty((w.M, w.D), dtype=dtype, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+    if args.which == "backward":
+        return bench_backward(args, w, inp, X, shards, dtype, dev)
 
     def step(events=None):
         tp.tp_mlp(X, shards, layernorm=w.layernorm, residual=residual, out=Y, events=events)

@@ -241,11 +241,12 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, eps: flo
     return out
 
 
-def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards):
+def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards, out=None):
     """Gradients (dX, dA, dB) of the TP-MLP given dY = dL/dY (tpmlp_backward).
 
     dA has A's layout (D x F, shard i in its columns), dB has B's (F x D,
-    shard i in its rows); all three in the weights' dtype.
+    shard i in its rows); all three in the weights' dtype.  `out` may give
+    the three result tensors.
     """
     if X.dim() != 2 or X.shape[1] != shards.D:
         raise ValueError(f"X must be (M, {shards.D})")
@@ -254,9 +255,15 @@ def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards):
     if tuple(dY.shape) != tuple(X.shape):
         raise ValueError("dY must have X's shape")
     M = X.shape[0]
-    dX = torch.empty_like(X)
-    dA = torch.empty((shards.D, shards.F), dtype=shards.dtype, device=X.device)
-    dB = torch.empty((shards.F, shards.D), dtype=shards.dtype, device=X.device)
+    if out is None:
+        dX = torch.empty_like(X)
+        dA = torch.empty((shards.D, shards.F), dtype=shards.dtype, device=X.device)
+        dB = torch.empty((shards.F, shards.D), dtype=shards.dtype, device=X.device)
+    else:
+        dX, dA, dB = out
+        want = ((M, shards.D), (shards.D, shards.F), (shards.F, shards.D))
+        if any(tuple(t.shape) != sh or t.dtype != shards.dtype for t, sh in zip((dX, dA, dB), want)):
+            raise ValueError("out tensors have the wrong shape or dtype")
     L = lib()
     nbytes = L.tpmlp_backward_workspace_bytes(shards.handle, M)
     ws = shards.workspace(nbytes)
