@@ -181,6 +181,9 @@ typedef struct {
     void* const* events;       /* optional: 4 hipEvent_t recorded on the stream before the
                                   LayerNorm statistics, before the first GEMM, between the
                                   GEMMs and after the second GEMM (NULL entries skipped)      */
+    void* save_preact;         /* optional M x F (M x F/n with shard_index), weights' dtype:
+                                  receives the pre-activation S = X A (after the LayerNorm
+                                  correction) for tpmlp_backward                              */
 } tpmlp_opts;
 
 /* Fills *o with the defaults described above. */
@@ -218,11 +221,14 @@ size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M);
  *   dX = sum_i dS_i A_i^T,
  * the last sum being the backward all-reduce of "LLM Lab Notes 06", section
  * 2, marker 1 and the ledger of section 3 (formed here in one fp32
- * accumulator, like the forward's).  S is recomputed from X; S, H and dS are
- * held in the weights' dtype between the GEMMs.
+ * accumulator, like the forward's).  S, H and dS are held in the weights'
+ * dtype between the GEMMs.
  *   X, dY  device, M x D row-major, the descriptor's dtype.
  *   M      rows; 0 gives dX nothing to write and zero dA, dB.
  *   s      descriptor from tpmlp_shard (its packed weights are read only).
+ *   preact optional M x F pre-activation S = X A saved by a forward without
+ *          LayerNorm over all shards (tpmlp_opts.save_preact); NULL recomputes
+ *          it (one more GEMM of 2 M D F).
  *   dX     device, M x D, the descriptor's dtype.
  *   dA     device, D x F: dA_i in columns iF/n .. (i+1)F/n - 1 (A's layout).
  *   dB     device, F x D: dB_i in rows iF/n .. (i+1)F/n - 1 (B's layout).
@@ -233,8 +239,8 @@ size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M);
  * TPMLP_ERR_ALIGN, TPMLP_ERR_WORKSPACE, TPMLP_ERR_HIP; all but the last are
  * returned before any HIP call.
  */
-tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpmlp_shards* s, void* dX, void* dA,
-                            void* dB, void* workspace, size_t workspace_bytes, void* stream);
+tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpmlp_shards* s, const void* preact,
+                            void* dX, void* dA, void* dB, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

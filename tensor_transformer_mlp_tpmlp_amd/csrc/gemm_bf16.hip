@@ -85,6 +85,7 @@ struct FastParams {
     const float* csum;   // LayerNorm: per-column sums of Bop (= column sums of A)
     const bf16* aux;     // kEpiGeluGrad: pre-activation, M x N
     int64_t ldaux;
+    bf16* preact;        // kEpiGelu: optional copy of the pre-activation (C's layout)
     int tiles_m, tiles_n;
     int group;           // tile rows walked together on one XCD
     int nt_store;        // write C with non-temporal stores
@@ -377,6 +378,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
             }
         }
         if constexpr (EPI == kEpiGelu) {
+            if (p.preact) {
+                // the pre-activation, kept for a backward pass
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(v[j][r]);
+                    bf16x4* dst = reinterpret_cast<bf16x4*>(p.preact + m * p.ldc + n_base + j * 16);
+                    if (p.nt_store) __builtin_nontemporal_store(o, dst);
+                    else *dst = o;
+                }
+            }
             gelu_tanh_staged(v);
         } else if constexpr (EPI == kEpiGeluGrad) {
 #pragma unroll
@@ -429,6 +442,7 @@ hipError_t launch_typed(const GemmArgs& g, int splits, hipStream_t stream) {
     p.R = static_cast<const bf16*>(g.R); p.ldr = g.ldr;
     p.mean = g.ln_mean; p.rstd = g.ln_rstd; p.csum = g.ln_csum;
     p.aux = static_cast<const bf16*>(g.aux); p.ldaux = g.ldaux;
+    p.preact = static_cast<bf16*>(g.preact_out);
     p.tiles_m = (int)(g.M / BM);
     p.tiles_n = (int)(g.N / BN);
     p.group = 4;
@@ -481,6 +495,7 @@ static bool fits_tile(const GemmArgs& g, int wb) {
     if (g.epi == kEpiGeluGrad && (!g.aux || g.ldaux % 4 || (reinterpret_cast<uintptr_t>(g.aux) & 7) ||
                                   g.c_dtype != kBF16))
         return false;
+    if (g.preact_out && (reinterpret_cast<uintptr_t>(g.preact_out) & 7)) return false;
     return true;
 }
 

@@ -34,6 +34,7 @@ struct GenericParams {
     const float* rstd;
     const void* aux;     // kEpiGeluGrad: pre-activation, operand dtype
     int64_t ldaux;
+    void* preact;        // kEpiGelu: optional copy of the pre-activation (C's layout and dtype)
     int64_t tiles_n;
 };
 
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GenericParams p) {
         if (m < p.M && n < p.N) {
             float v = acc[r];
             if constexpr (EPI == kEpiGelu) {
+                if (p.preact) static_cast<TC*>(p.preact)[m * p.ldc + n] = from_f32<TC>(v);
                 v = gelu_tanh(v);
             } else if constexpr (EPI == kEpiGeluGrad) {
                 v *= gelu_tanh_grad(to_f32(static_cast<const T*>(p.aux)[m * p.ldaux + n]));
@@ -127,6 +129,7 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
     p.C = g.C; p.ldc = g.ldc; p.R = g.R; p.ldr = g.ldr;
     p.mean = g.ln_mean; p.rstd = g.ln_rstd;
     p.aux = g.aux; p.ldaux = g.ldaux;
+    p.preact = g.preact_out;
     p.tiles_n = (g.N + GT - 1) / GT;
     const int64_t tiles = ((g.M + GT - 1) / GT) * p.tiles_n;
     if (g.ln_mean)

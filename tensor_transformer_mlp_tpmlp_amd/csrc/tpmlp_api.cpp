@@ -277,7 +277,9 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
     if (!(eps < 1e30f)) return TPMLP_ERR_SHAPE;
     if (M == 0) return TPMLP_OK;
     if (!X || !Y) return TPMLP_ERR_NULL;
-    if (!aligned16(X) || !aligned16(Y) || (o.residual && !aligned16(o.residual))) return TPMLP_ERR_ALIGN;
+    if (!aligned16(X) || !aligned16(Y) || (o.residual && !aligned16(o.residual)) ||
+        (o.save_preact && !aligned16(o.save_preact)))
+        return TPMLP_ERR_ALIGN;
 
     const bool single = o.shard_index >= 0;
     void* ws = o.workspace ? o.workspace : s->ws;
@@ -319,6 +321,7 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
         g1.ln_csum = ln ? csum + n_lo : nullptr;
         g1.epi = kEpiGelu;
         g1.ab_dtype = s->dtype;
+        g1.preact_out = o.save_preact;
         e = launch_gemm(g1, hs);
     }
     if (e == hipSuccess) e = mark(2);
@@ -351,12 +354,13 @@ size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M) {
     return bwd_layout(s, M).total;
 }
 
-tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpmlp_shards* s, void* dX, void* dA,
-                            void* dB, void* workspace, size_t workspace_bytes, void* stream) {
+tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpmlp_shards* s, const void* preact,
+                            void* dX, void* dA, void* dB, void* workspace, size_t workspace_bytes, void* stream) {
     if (!s) return TPMLP_ERR_NULL;
     if (M < 0 || M > kMaxDim) return TPMLP_ERR_SHAPE;
     if (!dA || !dB || (M > 0 && (!X || !dY || !dX))) return TPMLP_ERR_NULL;
-    if (!aligned16(dA) || !aligned16(dB) || (M > 0 && (!aligned16(X) || !aligned16(dY) || !aligned16(dX))))
+    if (!aligned16(dA) || !aligned16(dB) || (M > 0 && (!aligned16(X) || !aligned16(dY) || !aligned16(dX))) ||
+        (preact && !aligned16(preact)))
         return TPMLP_ERR_ALIGN;
     const BwdLayout L = bwd_layout(s, M);
     if (!workspace || workspace_bytes < L.total) return TPMLP_ERR_WORKSPACE;
@@ -404,11 +408,12 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
     // The weights in their own layouts ("The split": A is D x F, B is F x D).
     hipError_t e = launch_transpose(at, D, Aw, F, F, D, eb, hs);
     if (e == hipSuccess) e = launch_transpose(bt, F, Bw, D, D, F, eb, hs);
-    // S = X A for all shards at once; H = GeLU(S)
-    if (e == hipSuccess) e = gemm(X, D, at, D, M, F, D, S, F, kEpiStore, nullptr);
-    if (e == hipSuccess) e = launch_gelu(S, H, M * F, dt, hs);
+    // S = X A for all shards at once, unless the forward kept it; H = GeLU(S)
+    const void* Sv = preact ? preact : S;
+    if (e == hipSuccess && !preact) e = gemm(X, D, at, D, M, F, D, S, F, kEpiStore, nullptr);
+    if (e == hipSuccess) e = launch_gelu(Sv, H, M * F, dt, hs);
     // dS = (dY B^T) * GeLU'(S): the gradient at every shard's GeLU input
-    if (e == hipSuccess) e = gemm(dY, D, Bw, D, M, F, D, dS, F, kEpiGeluGrad, S);
+    if (e == hipSuccess) e = gemm(dY, D, Bw, D, M, F, D, dS, F, kEpiGeluGrad, Sv);
     // dX = sum_i dS_i A_i^T: the K loop over F sums the shards in registers
     if (e == hipSuccess) e = gemm(dS, F, Aw, F, M, D, F, dX, D, kEpiStore, nullptr);
     // dA = X^T dS and dB = H^T dY: K = M, from transposed copies

@@ -36,7 +36,7 @@ class Opts(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_int), ("ln_eps", ctypes.c_float), ("y_dtype", ctypes.c_int),
                 ("residual", ctypes.c_void_p), ("shard_index", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("events", ctypes.c_void_p)]
+                ("events", ctypes.c_void_p), ("save_preact", ctypes.c_void_p)]
 
 
 SIGNATURES = {
@@ -57,7 +57,7 @@ SIGNATURES = {
     "tpmlp_opts_init": (None, [ctypes.POINTER(Opts)]),
     "tpmlp_forward_ex": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, ctypes.POINTER(Opts), _c_vp]),
     "tpmlp_backward_workspace_bytes": (_c_sz, [_c_vp, _c_i64]),
-    "tpmlp_backward": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "tpmlp_backward": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
 }
 
 _lib = None
@@ -198,12 +198,15 @@ def shard_mlp(A: torch.Tensor, B: torch.Tensor, n: int) -> Shards:
 def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, eps: float = 1e-5,
            residual: Optional[torch.Tensor] = None, shard_index: int = -1,
            out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-           events: Optional[Sequence[int]] = None) -> torch.Tensor:
+           events: Optional[Sequence[int]] = None,
+           save_preact: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = sum_i GeLU(X A_i) B_i on the GPU (tpmlp_forward_ex).
 
     layernorm: normalise each row of X first (no affine); residual: added once
     after the shard sum; shard_index: return only partial Y_i; events: four
-    hipEvent_t handles recorded around the kernels (timing hook).
+    hipEvent_t handles recorded around the kernels (timing hook);
+    save_preact: an (M, F) tensor (F/n with shard_index) of the weights'
+    dtype that receives the pre-activation X A for tp_mlp_backward.
     """
     if X.dim() != 2 or X.shape[1] != shards.D:
         raise ValueError(f"X must be (M, {shards.D})")
@@ -229,6 +232,11 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, eps: flo
             raise ValueError("residual must match X")
         o.residual = _dev(residual, "residual")
     o.shard_index = shard_index
+    if save_preact is not None:
+        nh = shards.F // shards.n if shard_index >= 0 else shards.F
+        if save_preact.dtype != shards.dtype or tuple(save_preact.shape) != (M, nh):
+            raise ValueError(f"save_preact must be ({M}, {nh}) with the weights' dtype")
+        o.save_preact = _dev(save_preact, "save_preact")
     o.workspace = ws.data_ptr()
     o.workspace_bytes = ws.numel()
     ev_arr = None
@@ -241,12 +249,14 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, eps: flo
     return out
 
 
-def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards, out=None):
+def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards, out=None,
+                    preact: Optional[torch.Tensor] = None):
     """Gradients (dX, dA, dB) of the TP-MLP given dY = dL/dY (tpmlp_backward).
 
     dA has A's layout (D x F, shard i in its columns), dB has B's (F x D,
     shard i in its rows); all three in the weights' dtype.  `out` may give
-    the three result tensors.
+    the three result tensors; `preact` the (M, F) pre-activation a forward
+    kept with save_preact (otherwise it is recomputed).
     """
     if X.dim() != 2 or X.shape[1] != shards.D:
         raise ValueError(f"X must be (M, {shards.D})")
@@ -264,10 +274,15 @@ def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards, out=None)
         want = ((M, shards.D), (shards.D, shards.F), (shards.F, shards.D))
         if any(tuple(t.shape) != sh or t.dtype != shards.dtype for t, sh in zip((dX, dA, dB), want)):
             raise ValueError("out tensors have the wrong shape or dtype")
+    pp = None
+    if preact is not None:
+        if preact.dtype != shards.dtype or tuple(preact.shape) != (M, shards.F):
+            raise ValueError(f"preact must be ({M}, {shards.F}) with the weights' dtype")
+        pp = _dev(preact, "preact") if M else None
     L = lib()
     nbytes = L.tpmlp_backward_workspace_bytes(shards.handle, M)
     ws = shards.workspace(nbytes)
     _check(L.tpmlp_backward(_dev(X, "X") if M else X.data_ptr(), _dev(dY, "dY") if M else dY.data_ptr(), M,
-                            shards.handle, _dev(dX, "dX") if M else dX.data_ptr(), _dev(dA, "dA"),
+                            shards.handle, pp, _dev(dX, "dX") if M else dX.data_ptr(), _dev(dA, "dA"),
                             _dev(dB, "dB"), ws.data_ptr(), ws.numel(), _stream(X.device)), "tpmlp_backward")
     return dX, dA, dB

@@ -130,14 +130,14 @@ def test_backward_errors_with_real_descriptor():
     need = L.tpmlp_backward_workspace_bytes(sh.handle, 64)
     assert need > 0
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    args = (X.data_ptr(), tdY.data_ptr(), 64, sh.handle, dX.data_ptr(), dA.data_ptr(), dB.data_ptr())
+    args = (X.data_ptr(), tdY.data_ptr(), 64, sh.handle, None, dX.data_ptr(), dA.data_ptr(), dB.data_ptr())
     assert L.tpmlp_backward(*args, ws.data_ptr(), need - 1, None) == 5      # workspace too small
     assert L.tpmlp_backward(*args, None, need, None) == 5
-    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), -1, sh.handle, dX.data_ptr(), dA.data_ptr(),
+    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), -1, sh.handle, None, dX.data_ptr(), dA.data_ptr(),
                             dB.data_ptr(), ws.data_ptr(), need, None) == 2
-    assert L.tpmlp_backward(X.data_ptr() + 4, tdY.data_ptr(), 64, sh.handle, dX.data_ptr(), dA.data_ptr(),
+    assert L.tpmlp_backward(X.data_ptr() + 4, tdY.data_ptr(), 64, sh.handle, None, dX.data_ptr(), dA.data_ptr(),
                             dB.data_ptr(), ws.data_ptr(), need, None) == 6
-    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), 64, sh.handle, dX.data_ptr(), None,
+    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), 64, sh.handle, None, dX.data_ptr(), None,
                             dB.data_ptr(), ws.data_ptr(), need, None) == 1
     assert L.tpmlp_backward(*args, ws.data_ptr(), need, None) == 0
     torch.cuda.synchronize()
@@ -145,3 +145,26 @@ def test_backward_errors_with_real_descriptor():
     assert_close(to_f64(dX), rX, "f32", "dX")
     assert_close(to_f64(dA), rA, "f32", "dA")
     assert_close(to_f64(dB), rB, "f32", "dB")
+
+
+@pytest.mark.parametrize("M,D,F,n,dtype", [(512, 256, 1024, 4, "bf16"), (130, 70, 96, 3, "f32")])
+def test_forward_saves_preact_and_backward_uses_it(M, D, F, n, dtype):
+    """save_preact returns S = X A (the oracle's, to the dtype's tolerance), and
+    a backward given that S is bit-identical to one that recomputes it (the
+    same GEMM produces both)."""
+    say(f"save_preact M={M} D={D} F={F} n={n} {dtype}")
+    inp, dY = _case(M, D, F, seed=4242 + M, dtype=dtype)
+    dt = torch_dtype(dtype)
+    X, A, B, tdY = (to_dev(a, dt) for a in (inp.X, inp.A, inp.B, dY))
+    sh = tp.shard_mlp(A, B, n)
+    S = torch.empty((M, F), dtype=dt, device="cuda")
+    Y = tp.tp_mlp(X, sh, save_preact=S)
+    torch.cuda.synchronize()
+    assert_close(to_f64(S), inp.X.astype(np.float64) @ inp.A.astype(np.float64), dtype, "saved pre-activation")
+    assert_close(to_f64(Y), oracle.tp_mlp(inp.X, oracle.shard_mlp(inp.A, inp.B, n)), dtype, "forward with save")
+    with_s = tp.tp_mlp_backward(X, tdY, sh, preact=S)
+    torch.cuda.synchronize()
+    without = tp.tp_mlp_backward(X, tdY, sh)
+    torch.cuda.synchronize()
+    for a, b in zip(with_s, without):
+        assert torch.equal(a, b)
