@@ -206,9 +206,9 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
 
 /*
  * Bytes of device workspace tpmlp_backward needs for M rows: the weights
- * unpacked to A (D x F) and B (F x D), three M x F intermediates (S = X A,
- * H = GeLU(S) and dS), transposed copies of X and dY (D x M each), all in
- * the weights' dtype, plus the split-K scratch of its GEMMs.  Returns 0 for
+ * unpacked to A (D x F) and B (F x D), three M x F intermediates (S = X A
+ * then dS^T, H^T = GeLU(S)^T, and dS), transposed copies of X and dY (D x M
+ * each), all in the weights' dtype, plus the split-K scratch of its GEMMs.  Returns 0 for
  * invalid arguments.
  */
 size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M);

@@ -123,16 +123,107 @@ hipError_t launch_rowsum(const void* x, int64_t rows, int64_t cols, int dtype, f
 }
 
 // ---------------------------------------------------------------------------
-// Strided transpose out[c][r] = in[r][c] (r < R, c < C), bit-exact, through a
-// 64x64 LDS tile padded by one element against bank conflicts.  Used to pack
-// A (D x F) into K-contiguous A^T (F x D) and B (F x D) into B^T (D x F), and
-// to unpack a shard back into the page's layout.
+// Strided transpose out[c][r] = f(in[r][c]) (r < R, c < C), with f the
+// identity (bit-exact) or the tanh GeLU ("Tensor-Parallel MLP (Megatron)",
+// section "GeLU").  Used to pack A (D x F) into K-contiguous A^T (F x D) and
+// B (F x D) into B^T (D x F), to unpack a shard, and in the backward to lay
+// the activations out with the batch axis contiguous (the weight gradients
+// contract over it).
+//
+// Vector form: V = 16 / sizeof(T) elements per 16-byte chunk, a tile of 16V x
+// 16V elements per block of 256 threads.  Every global access is a 16-byte
+// chunk (a wave reads 4 rows x 256 contiguous bytes per load and writes 4 rows
+// x 256 contiguous bytes per store).  Phase 1 stores the chunks in LDS,
+// chunk slot = chunk ^ (row / V % 16); phase 2 gives thread (a, b) the V x V
+// block at rows aV.., columns bV..: it reads V chunks of one slot column
+// (16 lanes of a pass hit 16 distinct 16-byte slots, so no bank conflict),
+// transposes the block in registers and writes V output chunks.  Requires R,
+// C, ldi, ldo to be multiples of V and 16-byte aligned pointers; other shapes
+// take the element-wise form below.
 // ---------------------------------------------------------------------------
-template <typename E>
-__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ in, int64_t ldi,
-                                                        E* __restrict__ out, int64_t ldo, int64_t R,
+template <typename T, bool GELU>
+__device__ __forceinline__ u32x4 apply_chunk(u32x4 v) {
+    if constexpr (!GELU) {
+        return v;
+    } else {
+        constexpr int V = 16 / sizeof(T);
+        T vals[V];
+        __builtin_memcpy(vals, &v, 16);
+#pragma unroll
+        for (int e = 0; e < V; ++e) vals[e] = from_f32<T>(gelu_tanh(to_f32(vals[e])));
+        __builtin_memcpy(&v, vals, 16);
+        return v;
+    }
+}
+
+// x[i] holds row i of a V x V block as V elements packed in 4 dwords; y[c]
+// receives column c.  For 4-byte elements this is a renaming of dwords; for
+// 2-byte elements each output dword pairs the same half of two input dwords.
+template <int V>
+__device__ __forceinline__ void transpose_block(const u32x4 (&x)[V], u32x4 (&y)[V]);
+
+template <>
+__device__ __forceinline__ void transpose_block<4>(const u32x4 (&x)[4], u32x4 (&y)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[c][k] = x[k][c];
+}
+
+template <>
+__device__ __forceinline__ void transpose_block<8>(const u32x4 (&x)[8], u32x4 (&y)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = x[2 * k][j], hi = x[2 * k + 1][j];
+            y[2 * j][k] = (lo & 0xffffu) | (hi << 16);
+            y[2 * j + 1][k] = (lo >> 16) | (hi & 0xffff0000u);
+        }
+}
+
+template <typename T, bool GELU>
+__global__ __launch_bounds__(256) void transpose_vec_kernel(const T* __restrict__ in, int64_t ldi,
+                                                            T* __restrict__ out, int64_t ldo, int64_t R,
+                                                            int64_t C) {
+    constexpr int V = 16 / sizeof(T);
+    constexpr int TR = 16 * V;  // tile rows = tile columns
+    __shared__ u32x4 tile[TR * 16];
+    const int64_t r0 = (int64_t)blockIdx.y * TR;
+    const int64_t c0 = (int64_t)blockIdx.x * TR;
+    const int t = threadIdx.x;
+    const int ch = t & 15;
+    const bool col_ok = c0 + (int64_t)ch * V < C;
+#pragma unroll
+    for (int p = 0; p < V; ++p) {
+        const int row = (t >> 4) + 16 * p;
+        if (col_ok && r0 + row < R) {
+            const u32x4 v = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(in + (r0 + row) * ldi + c0 + (int64_t)ch * V));
+            tile[row * 16 + (ch ^ ((row / V) & 15))] = apply_chunk<T, GELU>(v);
+        }
+    }
+    __syncthreads();
+    const int a = t & 15;  // block row: input rows aV .. aV+V-1
+    const int b = t >> 4;  // block column: input columns bV .. bV+V-1
+    if (r0 + (int64_t)a * V >= R || c0 + (int64_t)b * V >= C) return;
+    u32x4 x[V], y[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) x[i] = tile[(a * V + i) * 16 + (b ^ a)];
+    transpose_block<V>(x, y);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        __builtin_nontemporal_store(
+            y[i], reinterpret_cast<u32x4*>(out + (c0 + (int64_t)b * V + i) * ldo + r0 + (int64_t)a * V));
+}
+
+// Element-wise form for any shape and alignment: a 64 x 64 tile, one element
+// per thread and access, LDS padded by one element per row.
+template <typename T, bool GELU>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int64_t ldi,
+                                                        T* __restrict__ out, int64_t ldo, int64_t R,
                                                         int64_t C) {
-    __shared__ E tile[64][65];
+    __shared__ T tile[64][65];
     const int64_t r0 = (int64_t)blockIdx.y * 64;
     const int64_t c0 = (int64_t)blockIdx.x * 64;
     const int tx = threadIdx.x & 63;
@@ -140,7 +231,11 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ in
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int rr = ty + 4 * i;
-        if (r0 + rr < R && c0 + tx < C) tile[rr][tx] = in[(r0 + rr) * ldi + c0 + tx];
+        if (r0 + rr < R && c0 + tx < C) {
+            T v = in[(r0 + rr) * ldi + c0 + tx];
+            if constexpr (GELU) v = from_f32<T>(gelu_tanh(to_f32(v)));
+            tile[rr][tx] = v;
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -150,16 +245,35 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ in
     }
 }
 
+template <typename T, bool GELU>
+static hipError_t transpose_typed(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
+                                  hipStream_t stream) {
+    constexpr int64_t V = 16 / sizeof(T);
+    const bool vec = R % V == 0 && C % V == 0 && ldi % V == 0 && ldo % V == 0 &&
+                     reinterpret_cast<uintptr_t>(in) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0;
+    const T* src = static_cast<const T*>(in);
+    T* dst = static_cast<T*>(out);
+    if (vec) {
+        const dim3 grid((unsigned)((C + 16 * V - 1) / (16 * V)), (unsigned)((R + 16 * V - 1) / (16 * V)));
+        transpose_vec_kernel<T, GELU><<<grid, dim3(256), 0, stream>>>(src, ldi, dst, ldo, R, C);
+    } else {
+        const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
+        transpose_kernel<T, GELU><<<grid, dim3(256), 0, stream>>>(src, ldi, dst, ldo, R, C);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_transpose(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
                             int elem_bytes, hipStream_t stream) {
-    const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-    if (elem_bytes == 4)
-        transpose_kernel<uint32_t><<<grid, dim3(256), 0, stream>>>(
-            static_cast<const uint32_t*>(in), ldi, static_cast<uint32_t*>(out), ldo, R, C);
-    else
-        transpose_kernel<uint16_t><<<grid, dim3(256), 0, stream>>>(
-            static_cast<const uint16_t*>(in), ldi, static_cast<uint16_t*>(out), ldo, R, C);
-    return hipGetLastError();
+    // bit-exact copies: the element's type only sets its width
+    return elem_bytes == 4 ? transpose_typed<float, false>(in, ldi, out, ldo, R, C, stream)
+                           : transpose_typed<bf16, false>(in, ldi, out, ldo, R, C, stream);
+}
+
+hipError_t launch_transpose_gelu(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
+                                 int dtype, hipStream_t stream) {
+    return dtype == kF32 ? transpose_typed<float, true>(in, ldi, out, ldo, R, C, stream)
+                         : transpose_typed<bf16, true>(in, ldi, out, ldo, R, C, stream);
 }
 
 }  // namespace tpmlp

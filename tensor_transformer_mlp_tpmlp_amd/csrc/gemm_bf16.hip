@@ -361,9 +361,30 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // independent GeLU chains to interleave.
     TC* __restrict__ C = static_cast<TC*>(p.C) + kz * p.c_split_stride;
     const int64_t n_base = n0 + wn * 16 * NB + 4 * (lane >> 4);
+    const int64_t m_base = m0 + wm * 16 * NB + (lane & 15);
+    // The epilogue's operand (the pre-activation, or the residual) is read
+    // for the whole wave tile before the first row block is transformed, so
+    // its memory latency is paid once rather than once per row block.
+    constexpr bool kHasAux = EPI != kEpiGelu;
+    bf16x4 ex[kHasAux ? NB : 1][kHasAux ? NB : 1];
+    if constexpr (EPI == kEpiGeluGrad) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                ex[i][j] = *reinterpret_cast<const bf16x4*>(p.aux + (m_base + i * 16) * p.ldaux + n_base + j * 16);
+    } else if constexpr (EPI == kEpiStore) {
+        if (p.R) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    ex[i][j] = *reinterpret_cast<const bf16x4*>(p.R + (m_base + i * 16) * p.ldr + n_base + j * 16);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        const int64_t m = m0 + wm * 16 * NB + i * 16 + (lane & 15);
+        const int64_t m = m_base + i * 16;
         f32x4 v[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) v[j] = acc[i][j];
@@ -393,19 +414,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
             gelu_tanh_staged(v);
         } else if constexpr (EPI == kEpiGeluGrad) {
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const bf16x4 sv = *reinterpret_cast<const bf16x4*>(p.aux + m * p.ldaux + n_base + j * 16);
+            for (int j = 0; j < NB; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[j][r] *= gelu_tanh_grad(static_cast<float>(sv[r]));
-            }
+                for (int r = 0; r < 4; ++r) v[j][r] *= gelu_tanh_grad(static_cast<float>(ex[i][j][r]));
         } else {
             if (p.R) {
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const bf16x4 rv = *reinterpret_cast<const bf16x4*>(p.R + m * p.ldr + n_base + j * 16);
+                for (int j = 0; j < NB; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) v[j][r] += static_cast<float>(rv[r]);
-                }
+                    for (int r = 0; r < 4; ++r) v[j][r] += static_cast<float>(ex[i][j][r]);
             }
         }
         // A large output (H of the big workloads) is written non-temporally:

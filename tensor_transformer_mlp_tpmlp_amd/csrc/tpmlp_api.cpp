@@ -102,10 +102,10 @@ GemmArgs bwd_shape(int64_t M, int64_t N, int64_t K, int dtype) {
 
 // Backward workspace, each segment 256-byte aligned:
 //   A (D x F) and B (F x D) unpacked from the shard buffer,
-//   S = X A (M x F), later H^T (F x M);  H = GeLU(S) (M x F), later dS^T;
+//   S = X A (M x F), later dS^T (F x M);  H^T = GeLU(S)^T (F x M);
 //   dS (M x F);  X^T (D x M);  dY^T (D x M);  split-K scratch.
 struct BwdLayout {
-    size_t a, b, s_ht, h_dst, ds, xt, dyt, split, split_bytes, total;
+    size_t a, b, s_dst, ht, ds, xt, dyt, split, split_bytes, total;
 };
 
 BwdLayout bwd_layout(const tpmlp_shards* s, int64_t M) {
@@ -115,8 +115,8 @@ BwdLayout bwd_layout(const tpmlp_shards* s, int64_t M) {
     size_t off = 0;
     L.a = off; off += round_up(D * F * es);
     L.b = off; off += round_up(F * D * es);
-    L.s_ht = off; off += round_up(m * F * es);
-    L.h_dst = off; off += round_up(m * F * es);
+    L.s_dst = off; off += round_up(m * F * es);
+    L.ht = off; off += round_up(m * F * es);
     L.ds = off; off += round_up(m * F * es);
     L.xt = off; off += round_up(D * m * es);
     L.dyt = off; off += round_up(D * m * es);
@@ -399,8 +399,8 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
 
     void* Aw = w + L.a;        // A: D x F
     void* Bw = w + L.b;        // B: F x D
-    void* S = w + L.s_ht;      // S: M x F, later H^T: F x M
-    void* H = w + L.h_dst;     // H: M x F, later dS^T: F x M
+    void* S = w + L.s_dst;      // S: M x F, later dS^T: F x M
+    void* Ht = w + L.ht;    // H^T: F x M
     void* dS = w + L.ds;       // dS: M x F
     void* Xt = w + L.xt;       // X^T: D x M
     void* dYt = w + L.dyt;     // dY^T: D x M
@@ -408,21 +408,21 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
     // The weights in their own layouts ("The split": A is D x F, B is F x D).
     hipError_t e = launch_transpose(at, D, Aw, F, F, D, eb, hs);
     if (e == hipSuccess) e = launch_transpose(bt, F, Bw, D, D, F, eb, hs);
-    // S = X A for all shards at once, unless the forward kept it; H = GeLU(S)
+    // S = X A for all shards at once, unless the forward kept it
     const void* Sv = preact ? preact : S;
     if (e == hipSuccess && !preact) e = gemm(X, D, at, D, M, F, D, S, F, kEpiStore, nullptr);
-    if (e == hipSuccess) e = launch_gelu(Sv, H, M * F, dt, hs);
     // dS = (dY B^T) * GeLU'(S): the gradient at every shard's GeLU input
     if (e == hipSuccess) e = gemm(dY, D, Bw, D, M, F, D, dS, F, kEpiGeluGrad, Sv);
     // dX = sum_i dS_i A_i^T: the K loop over F sums the shards in registers
     if (e == hipSuccess) e = gemm(dS, F, Aw, F, M, D, F, dX, D, kEpiStore, nullptr);
-    // dA = X^T dS and dB = H^T dY: K = M, from transposed copies
-    if (e == hipSuccess) e = launch_transpose(H, F, S, M, M, F, eb, hs);      // H^T into S's space
-    if (e == hipSuccess) e = launch_transpose(dS, F, H, M, M, F, eb, hs);     // dS^T into H's space
+    // dA = X^T dS and dB = H^T dY contract over the batch axis M: operands
+    // with M contiguous; H^T = GeLU(S)^T comes straight from S
+    if (e == hipSuccess) e = launch_transpose_gelu(Sv, F, Ht, M, M, F, dt, hs);
+    if (e == hipSuccess) e = launch_transpose(dS, F, S, M, M, F, eb, hs);     // dS^T into S's space
     if (e == hipSuccess) e = launch_transpose(X, D, Xt, M, M, D, eb, hs);
     if (e == hipSuccess) e = launch_transpose(dY, D, dYt, M, M, D, eb, hs);
-    if (e == hipSuccess) e = gemm(Xt, M, H, M, D, F, M, dA, F, kEpiStore, nullptr);
-    if (e == hipSuccess) e = gemm(S, M, dYt, M, F, D, M, dB, D, kEpiStore, nullptr);
+    if (e == hipSuccess) e = gemm(Xt, M, S, M, D, F, M, dA, F, kEpiStore, nullptr);
+    if (e == hipSuccess) e = gemm(Ht, M, dYt, M, F, D, M, dB, D, kEpiStore, nullptr);
     return from_hip(e);
 }
 

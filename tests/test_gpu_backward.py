@@ -50,8 +50,10 @@ BWD_SHAPES = [
     (1, 2, 4, 2, "f32"),
     (3, 5, 7, 7, "f32"),
     (130, 70, 96, 3, "f32"),
+    (60, 36, 100, 5, "f32"),        # multiples of 4: vector transposes, ragged tiles
     (64, 64, 256, 4, "bf16"),
     (257, 129, 384, 4, "bf16"),     # odd sizes: the bounds-checked kernel
+    (200, 136, 264, 3, "bf16"),     # multiples of 8: vector transposes, ragged tiles
     (512, 256, 1024, 4, "bf16"),    # every GEMM on the 128x128 ring kernel
     (1024, 512, 2048, 2, "bf16"),
 ]
