@@ -10,6 +10,8 @@ from .tpmlp_oracle import (  # noqa: F401
     gelu_scalar,
     layer_norm,
     layer_norm_loops,
+    norm_after_ffn,
+    norm_after_ffn_loops,
     post_ln_ffn,
     shard_mlp,
     shard_outputs,

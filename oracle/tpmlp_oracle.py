@@ -15,7 +15,9 @@ matching rows into B_i ("Tensor-Parallel MLP (Megatron)", scratchllm,
 sections "The problem", "The split", "Requirements").  The optional Post-LN
 FFN half of a block, out = x + TP-MLP(LayerNorm(x)), follows the code
 walkthrough of "LLM Lab Notes 06: Building a Megatron-Style Transformer
-Block from Scratch", section 2, markers 5 to 7.
+Block from Scratch", section 2, markers 5 to 7; the other placement that
+page describes, out = LayerNorm(x + TP-MLP(x)) (residual first, then the
+Norm), is ``norm_after_ffn``.
 
 The backward pass of the same MLP (the gradients of a loss L given
 dY = dL/dY) follows from the chain rule applied to the forward as defined
@@ -151,6 +153,22 @@ def post_ln_ffn(x, shards, eps: float = LN_EPS) -> np.ndarray:
     return x + tp_mlp(layer_norm(x, eps), shards)
 
 
+def norm_after_ffn(x, shards, eps: float = LN_EPS) -> np.ndarray:
+    """FFN half with the LayerNorm after the residual: out = LayerNorm(x + TP-MLP(x)).
+
+    "LLM Lab Notes 06", section 2, the note on markers 2 and 5: the prose
+    describes the Post-LN order of the original Transformer, the residual
+    added first and the LayerNorm applied to the sum, and says the Pre-LN
+    order (normalise first, the code as printed and ``post_ln_ffn`` above)
+    differs only in where the Norm and the residual sit; section 5,
+    takeaway 2, contrasts the two.  Reading: the TP-MLP sees the raw x, the
+    shard sum (the all-reduce) comes before the residual as in the code,
+    and the LayerNorm is the same no-affine one over the hidden axis.
+    """
+    x = _f64(x)
+    return layer_norm(x + tp_mlp(x, shards), eps)
+
+
 def gelu_grad(x) -> np.ndarray:
     """Derivative of the tanh-GeLU of "Tensor-Parallel MLP (Megatron)",
     section "GeLU", in float64.
@@ -272,6 +290,13 @@ def layer_norm_loops(x, eps: float = LN_EPS):
         inv = 1.0 / math.sqrt(var + eps)
         out.append([(v - mu) * inv for v in row])
     return out
+
+
+def norm_after_ffn_loops(x, A, B, n: int, eps: float = LN_EPS):
+    """Pure-Python version of norm_after_ffn on nested lists (tiny inputs)."""
+    Y, _ = tp_mlp_loops(x, A, B, n)
+    z = [[float(a) + float(b) for a, b in zip(xr, yr)] for xr, yr in zip(x, Y)]
+    return layer_norm_loops(z, eps)
 
 
 def gelu_grad_scalar(x: float) -> float:

@@ -177,6 +177,31 @@ def pin_post_ln(post_fn, shard_fn):
     return bool(ok)
 
 
+def pin_norm_after(after_fn, shard_fn):
+    """out = LayerNorm(x + TP-MLP(x)): the FFN sees the raw x, the residual
+    joins the shard sum, and the Norm comes last."""
+    inp = workloads.random_case(6, 32, 64, seed=12)
+    x, A, B = inp.X.astype(float), inp.A.astype(float) * 4.0, inp.B.astype(float) * 4.0
+    xt = torch.from_numpy(x)
+    F = torch.nn.functional
+    # B = 0 reduces to the library LayerNorm of x
+    ln_x = F.layer_norm(xt, (32,)).numpy()
+    ok = float(np.max(np.abs(after_fn(x, shard_fn(A, np.zeros_like(B), 4)) - ln_x))) <= 1e-12
+    # the whole composition with torch's layer_norm and tanh-GeLU
+    ref = F.layer_norm(xt + F.gelu(xt @ torch.from_numpy(A), approximate="tanh") @ torch.from_numpy(B),
+                       (32,)).numpy()
+    y4 = after_fn(x, shard_fn(A, B, 4))
+    ok &= float(np.max(np.abs(y4 - ref))) <= 1e-12
+    # any split gives the same result
+    ok &= float(np.max(np.abs(after_fn(x, shard_fn(A, B, 1)) - y4))) <= 1e-12
+    # every row normalised: mean 0, biased variance v / (v + eps) of the pre-Norm row
+    z = x + (F.gelu(xt @ torch.from_numpy(A), approximate="tanh") @ torch.from_numpy(B)).numpy()
+    v = z.var(axis=1)
+    ok &= bool(np.all(np.abs(y4.mean(axis=1)) <= 1e-12))
+    ok &= bool(np.all(np.abs(y4.var(axis=1) - v / (v + oracle.LN_EPS)) <= 1e-12))
+    return bool(ok)
+
+
 # ---------------------------------------------------------------------------
 # the oracle passes every pin
 # ---------------------------------------------------------------------------
@@ -286,6 +311,17 @@ def test_layer_norm():
 
 def test_post_ln_block():
     assert pin_post_ln(oracle.post_ln_ffn, oracle.shard_mlp)
+
+
+def test_norm_after_block():
+    assert pin_norm_after(oracle.norm_after_ffn, oracle.shard_mlp)
+    inp = workloads.random_case(3, 8, 12, seed=5)
+    x, A, B = inp.X.astype(float), inp.A.astype(float), inp.B.astype(float)
+    loops = np.array(oracle.norm_after_ffn_loops(x.tolist(), A.tolist(), B.tolist(), 3))
+    assert np.max(np.abs(loops - oracle.norm_after_ffn(x, oracle.shard_mlp(A, B, 3)))) <= 1e-13
+    # the two placements are different functions
+    sh = oracle.shard_mlp(A, B, 3)
+    assert np.max(np.abs(oracle.norm_after_ffn(x, sh) - oracle.post_ln_ffn(x, sh))) > 0.1
 
 
 # ---------------------------------------------------------------------------
@@ -403,3 +439,23 @@ def test_pins_reject_planted_mistakes():
 
     for bad in (post_normed_residual, post_per_shard):
         assert not pin_post_ln(bad, oracle.shard_mlp), bad.__name__
+
+    # Norm after the residual: normalising first, no residual, the residual
+    # outside the Norm, or the Norm taken per shard before the sum
+    def after_norm_first(x, shards):
+        return oracle.post_ln_ffn(x, shards)
+
+    def after_no_residual(x, shards):
+        return oracle.layer_norm(oracle.tp_mlp(x, shards))
+
+    def after_residual_outside(x, shards):
+        return np.asarray(x, float) + oracle.layer_norm(oracle.tp_mlp(x, shards))
+
+    def after_per_shard(x, shards):
+        _, Ys = oracle.shard_outputs(x, shards)
+        return sum(oracle.layer_norm(np.asarray(x, float) + Y) for Y in Ys) / len(Ys)
+
+    assert pin_norm_after(lambda x, sh: oracle.layer_norm(np.asarray(x, float) + oracle.tp_mlp(x, sh)),
+                          oracle.shard_mlp)
+    for bad in (after_norm_first, after_no_residual, after_residual_outside, after_per_shard):
+        assert not pin_norm_after(bad, oracle.shard_mlp), bad.__name__
