@@ -211,6 +211,8 @@ def cpu_baseline(w, inp, target_s: float):
         t0 = time.perf_counter()
         if w.layernorm:
             oracle.post_ln_ffn(x, shards)
+        elif w.layernorm_after:
+            oracle.norm_after_ffn(x, shards)
         else:
             oracle.tp_mlp(x, shards)
         return time.perf_counter() - t0
@@ -246,7 +248,7 @@ def bench_backward(args, w, inp, X, shards, dtype, dev) -> int:
     import tensor_transformer_mlp_tpmlp_amd as tp
     import workloads
 
-    if w.layernorm or w.residual:
+    if w.layernorm or w.residual or w.layernorm_after:
         raise SystemExit("the backward covers the TP-MLP without LayerNorm or residual")
     dYh = np.random.default_rng(w.seed + 7).standard_normal((w.M, w.D)).astype(np.float32)
     if w.dtype == "bf16":
@@ -353,7 +355,7 @@ def main() -> int:
         copy_calibration()
     dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     log(f"[bench] workload {w.name}: M={w.M} D={w.D} F={w.F} n={w.n} {w.dtype} "
-        f"layernorm={w.layernorm} residual={w.residual}")
+        f"layernorm={w.layernorm} residual={w.residual} layernorm_after={w.layernorm_after}")
     t0 = time.time()
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
@@ -368,7 +370,8 @@ def main() -> int:
         return bench_backward(args, w, inp, X, shards, dtype, dev)
 
     def step(events=None):
-        tp.tp_mlp(X, shards, layernorm=w.layernorm, residual=residual, out=Y, events=events)
+        tp.tp_mlp(X, shards, layernorm=w.layernorm, layernorm_after=w.layernorm_after, residual=residual,
+                  out=Y, events=events)
 
     for _ in range(args.warmup):
         step()
@@ -406,10 +409,10 @@ def main() -> int:
         "higher_is_better": True, "scaling": "strong", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "D": w.D, "F": w.F, "n": w.n,
-                   "layernorm": w.layernorm, "residual": w.residual},
+                   "layernorm": w.layernorm, "residual": w.residual, "layernorm_after": w.layernorm_after},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "kernels_ms": {"ln_stats": round(float(np.mean(t_ln)), 5), "gemm1_gelu": round(g1, 5),
-                       "gemm2_sum": round(g2, 5)},
+                       ("gemm2_sum_and_layernorm" if w.layernorm_after else "gemm2_sum"): round(g2, 5)},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -131,14 +131,16 @@ void tpmlp_shards_destroy(tpmlp_shards* s);
 
 /* Option flags for the forward workspace size and tpmlp_forward_ex. */
 enum {
-    TPMLP_OPT_LAYERNORM = 1      /* normalise each row of X first (no affine)  */
+    TPMLP_OPT_LAYERNORM = 1,       /* normalise each row of X first (no affine)       */
+    TPMLP_OPT_LAYERNORM_AFTER = 2  /* normalise each row of residual + Y last          */
 };
 
 /*
  * Bytes of device workspace a forward pass over M rows needs: the
  * intermediate H = GeLU(X A_i) for every shard (M x F, or M x F/n for a
  * single shard, in the weights' dtype) plus, with TPMLP_OPT_LAYERNORM, two
- * fp32 per-row statistics, plus fp32 partial sums (S x M x D) when the
+ * fp32 per-row statistics, plus, with TPMLP_OPT_LAYERNORM_AFTER, the
+ * M x D fp32 sum that is normalised, plus fp32 partial sums (S x M x D) when the
  * second GEMM has too few output tiles to fill the GPU and splits its
  * K loop S ways.  The size depends on the device's compute-unit count.
  * Returns 0 for invalid arguments.
@@ -171,7 +173,7 @@ tpmlp_status tpmlp_forward(const void* X, int64_t M, const tpmlp_shards* s, void
 
 /* Options of tpmlp_forward_ex.  Zero-initialise, then set what is needed. */
 typedef struct {
-    int flags;                 /* TPMLP_OPT_LAYERNORM or 0                                  */
+    int flags;                 /* 0, TPMLP_OPT_LAYERNORM or TPMLP_OPT_LAYERNORM_AFTER       */
     float ln_eps;              /* LayerNorm epsilon; 0 selects 1e-5                         */
     int y_dtype;               /* output dtype; -1 selects the descriptor's dtype            */
     const void* residual;      /* optional M x D, X's dtype: added once after the shard sum  */
@@ -180,7 +182,8 @@ typedef struct {
     size_t workspace_bytes;
     void* const* events;       /* optional: 4 hipEvent_t recorded on the stream before the
                                   LayerNorm statistics, before the first GEMM, between the
-                                  GEMMs and after the second GEMM (NULL entries skipped)      */
+                                  GEMMs and after the last kernel (the second GEMM, or the
+                                  final LayerNorm) (NULL entries skipped)                     */
     void* save_preact;         /* optional M x F (M x F/n with shard_index), weights' dtype:
                                   receives the pre-activation S = X A (after the LayerNorm
                                   correction) for tpmlp_backward                              */
@@ -198,6 +201,13 @@ void tpmlp_opts_init(tpmlp_opts* o);
  * variance in fp32), the residual x un-normalised and added once.
  * shard_index = i returns only GPU i's partial Y_i of section "The split",
  * bullet 2 (with a residual, the residual is added to that partial).
+ * With TPMLP_OPT_LAYERNORM_AFTER the Norm moves after the residual, the order
+ * of the original Transformer that the note on markers 2 and 5 of the same
+ * section describes (and section 5, takeaway 2, contrasts with Pre-LN):
+ * out = LayerNorm(residual + sum_i GeLU(X A_i) B_i), with X un-normalised;
+ * the sum is kept in fp32 and rounded once, after the Norm.  It cannot be
+ * combined with TPMLP_OPT_LAYERNORM or with shard_index >= 0 (the Norm
+ * needs the whole sum): TPMLP_ERR_SHAPE.
  * y_dtype may be TPMLP_F32 for bf16 weights (fp32 output); a bf16 output for
  * fp32 weights is TPMLP_ERR_DTYPE.
  */

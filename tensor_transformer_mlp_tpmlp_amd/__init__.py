@@ -10,6 +10,7 @@ from .tpmlp import (  # noqa: F401
     F32,
     LIB_PATH,
     OPT_LAYERNORM,
+    OPT_LAYERNORM_AFTER,
     Shards,
     TpmlpError,
     gelu,

@@ -82,15 +82,162 @@ __global__ __launch_bounds__(256) void ln_stats_kernel(const T* __restrict__ x, 
     }
 }
 
+// Register-resident form for rows of at most 64 * CH 16-byte chunks whose
+// length is a multiple of the chunk: the row is read once, with 16-byte
+// loads (a wave reads 1 KiB contiguous per load), and both passes (mean,
+// then squared deviations) run over registers.  With APPLY the wave also
+// writes the normalised row, (x - mean) * rstd rounded once to TO; without
+// it, it writes the two statistics.
+template <typename T, typename TO, int CH, bool APPLY>
+__global__ __launch_bounds__(256) void ln_rows_vec_kernel(const T* __restrict__ x, int64_t M, int64_t D,
+                                                          float eps, float* __restrict__ mean,
+                                                          float* __restrict__ rstd, TO* __restrict__ out) {
+    constexpr int V = 16 / sizeof(T);
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const T* xr = x + row * D;
+    float v[CH][V];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        const int64_t c = (int64_t)(lane + 64 * k) * V;
+        if (c < D) {
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + c);
+            T e[V];
+            __builtin_memcpy(e, &raw, 16);
+#pragma unroll
+            for (int r = 0; r < V; ++r) {
+                v[k][r] = to_f32(e[r]);
+                s += v[k][r];
+            }
+        }
+    }
+    const float mu = wave_sum(s) / (float)D;
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        if ((int64_t)(lane + 64 * k) * V < D) {
+#pragma unroll
+            for (int r = 0; r < V; ++r) {
+                const float d = v[k][r] - mu;
+                q = __builtin_fmaf(d, d, q);
+            }
+        }
+    }
+    const float var = wave_sum(q) / (float)D;
+    const float rs = 1.0f / __builtin_sqrtf(var + eps);
+    if constexpr (!APPLY) {
+        if (lane == 0) {
+            mean[row] = mu;
+            rstd[row] = rs;
+        }
+    } else {
+        TO* orow = out + row * D;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int64_t c = (int64_t)(lane + 64 * k) * V;
+            if (c < D) {
+                TO o[V];
+#pragma unroll
+                for (int r = 0; r < V; ++r) o[r] = from_f32<TO>((v[k][r] - mu) * rs);
+                if constexpr (sizeof(TO) * V == 16) {
+                    u32x4 w;
+                    __builtin_memcpy(&w, o, 16);
+                    *reinterpret_cast<u32x4*>(orow + c) = w;
+                } else {
+                    static_assert(sizeof(TO) * V == 8, "8- or 16-byte output chunks");
+                    uint2 w;
+                    __builtin_memcpy(&w, o, 8);
+                    *reinterpret_cast<uint2*>(orow + c) = w;
+                }
+            }
+        }
+    }
+}
+
+// Element-wise normalisation of an fp32 row for any length and alignment:
+// one wave per row, the same two statistics passes, then a writing pass.
+template <typename TO>
+__global__ __launch_bounds__(256) void ln_apply_kernel(const float* __restrict__ x, int64_t M, int64_t D,
+                                                       float eps, TO* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const float* xr = x + row * D;
+    float s = 0.f;
+    for (int64_t c = lane; c < D; c += 64) s += xr[c];
+    const float mu = wave_sum(s) / (float)D;
+    float q = 0.f;
+    for (int64_t c = lane; c < D; c += 64) {
+        const float d = xr[c] - mu;
+        q = __builtin_fmaf(d, d, q);
+    }
+    const float rs = 1.0f / __builtin_sqrtf(wave_sum(q) / (float)D + eps);
+    TO* orow = out + row * D;
+    for (int64_t c = lane; c < D; c += 64) orow[c] = from_f32<TO>((xr[c] - mu) * rs);
+}
+
+// Chunks per lane for the register-resident form (1, 2, 4 or 8), or 0 when
+// the row does not fit it.
+static int ln_chunks(int64_t D, int V, const void* x, const void* out) {
+    if (D % V != 0 || reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
+        return 0;
+    for (int ch = 1; ch <= 8; ch *= 2)
+        if (D <= (int64_t)64 * V * ch) return ch;
+    return 0;
+}
+
+template <typename T, typename TO, bool APPLY>
+static void launch_ln_vec(int ch, dim3 grid, const T* x, int64_t M, int64_t D, float eps, float* mean,
+                          float* rstd, TO* out, hipStream_t stream) {
+    switch (ch) {
+        case 1: ln_rows_vec_kernel<T, TO, 1, APPLY><<<grid, dim3(256), 0, stream>>>(x, M, D, eps, mean, rstd, out); break;
+        case 2: ln_rows_vec_kernel<T, TO, 2, APPLY><<<grid, dim3(256), 0, stream>>>(x, M, D, eps, mean, rstd, out); break;
+        case 4: ln_rows_vec_kernel<T, TO, 4, APPLY><<<grid, dim3(256), 0, stream>>>(x, M, D, eps, mean, rstd, out); break;
+        default: ln_rows_vec_kernel<T, TO, 8, APPLY><<<grid, dim3(256), 0, stream>>>(x, M, D, eps, mean, rstd, out); break;
+    }
+}
+
 hipError_t launch_ln_stats(const void* x, int64_t M, int64_t D, int dtype, float eps, float* mean,
                            float* rstd, hipStream_t stream) {
-    const int64_t blocks = (M + 3) / 4;
-    if (dtype == kF32)
-        ln_stats_kernel<float><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-            static_cast<const float*>(x), M, D, eps, mean, rstd);
-    else
-        ln_stats_kernel<bf16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-            static_cast<const bf16*>(x), M, D, eps, mean, rstd);
+    const dim3 grid((unsigned)((M + 3) / 4));
+    const int ch = ln_chunks(D, dtype == kF32 ? 4 : 8, x, x);
+    if (dtype == kF32) {
+        if (ch)
+            launch_ln_vec<float, float, false>(ch, grid, static_cast<const float*>(x), M, D, eps, mean, rstd,
+                                               nullptr, stream);
+        else
+            ln_stats_kernel<float><<<grid, dim3(256), 0, stream>>>(static_cast<const float*>(x), M, D, eps,
+                                                                   mean, rstd);
+    } else {
+        if (ch)
+            launch_ln_vec<bf16, float, false>(ch, grid, static_cast<const bf16*>(x), M, D, eps, mean, rstd,
+                                              nullptr, stream);
+        else
+            ln_stats_kernel<bf16><<<grid, dim3(256), 0, stream>>>(static_cast<const bf16*>(x), M, D, eps,
+                                                                  mean, rstd);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_ln_apply(const float* x, int64_t M, int64_t D, float eps, void* out, int out_dtype,
+                           hipStream_t stream) {
+    const dim3 grid((unsigned)((M + 3) / 4));
+    const int ch = ln_chunks(D, 4, x, out);
+    if (out_dtype == kF32) {
+        if (ch)
+            launch_ln_vec<float, float, true>(ch, grid, x, M, D, eps, nullptr, nullptr, static_cast<float*>(out),
+                                              stream);
+        else
+            ln_apply_kernel<float><<<grid, dim3(256), 0, stream>>>(x, M, D, eps, static_cast<float*>(out));
+    } else {
+        if (ch)
+            launch_ln_vec<float, bf16, true>(ch, grid, x, M, D, eps, nullptr, nullptr, static_cast<bf16*>(out),
+                                             stream);
+        else
+            ln_apply_kernel<bf16><<<grid, dim3(256), 0, stream>>>(x, M, D, eps, static_cast<bf16*>(out));
+    }
     return hipGetLastError();
 }
 

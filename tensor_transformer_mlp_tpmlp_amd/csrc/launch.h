@@ -58,6 +58,8 @@ hipError_t launch_gemm_bf16_fast(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gelu(const void* x, void* y, int64_t count, int dtype, hipStream_t stream);
 hipError_t launch_ln_stats(const void* x, int64_t M, int64_t D, int dtype, float eps, float* mean,
                            float* rstd, hipStream_t stream);
+hipError_t launch_ln_apply(const float* x, int64_t M, int64_t D, float eps, void* out, int out_dtype,
+                           hipStream_t stream);
 hipError_t launch_rowsum(const void* x, int64_t rows, int64_t cols, int dtype, float* out, hipStream_t stream);
 hipError_t launch_transpose(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
                             int elem_bytes, hipStream_t stream);

@@ -61,10 +61,12 @@ GemmArgs gemm2_shape(const tpmlp_shards* s, int64_t M, int64_t nh) {
 
 // Workspace layout for a forward over M rows with N_h intermediate columns:
 //   [H: M x N_h, weights' dtype][mean: M fp32][rstd: M fp32]
+//   [Z = residual + Y: M x D fp32, normalised last]
 //   [GEMM2 split-K partials: S x M x D fp32, when GEMM2 is split],
-// each segment 256-byte aligned.
+// each segment 256-byte aligned; the statistics exist only with the
+// LayerNorm before, Z only with the LayerNorm after.
 struct WsLayout {
-    size_t h_off, mean_off, rstd_off, split_off, split_bytes, total;
+    size_t h_off, mean_off, rstd_off, z_off, split_off, split_bytes, total;
 };
 
 WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard) {
@@ -79,6 +81,8 @@ WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard
         L.rstd_off = off;
         off += round_up((size_t)M * 4);
     }
+    L.z_off = off;
+    if (flags & TPMLP_OPT_LAYERNORM_AFTER) off += round_up((size_t)M * (size_t)s->D * 4);
     L.split_off = off;
     L.split_bytes = M > 0 ? gemm_split_bytes(gemm2_shape(s, M, nh)) : 0;
     off += round_up(L.split_bytes);
@@ -267,7 +271,9 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
     if (opts) o = *opts;
     if (!s) return TPMLP_ERR_NULL;
     if (M < 0 || M > kMaxDim) return TPMLP_ERR_SHAPE;
-    if (o.flags & ~TPMLP_OPT_LAYERNORM) return TPMLP_ERR_SHAPE;
+    if (o.flags & ~(TPMLP_OPT_LAYERNORM | TPMLP_OPT_LAYERNORM_AFTER)) return TPMLP_ERR_SHAPE;
+    const bool ln_after = (o.flags & TPMLP_OPT_LAYERNORM_AFTER) != 0;
+    if (ln_after && ((o.flags & TPMLP_OPT_LAYERNORM) || o.shard_index >= 0)) return TPMLP_ERR_SHAPE;
     const int y_dtype = o.y_dtype < 0 ? s->dtype : o.y_dtype;
     if (!valid_dtype(y_dtype)) return TPMLP_ERR_DTYPE;
     if (s->dtype == TPMLP_F32 && y_dtype != TPMLP_F32) return TPMLP_ERR_DTYPE;
@@ -327,13 +333,19 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
     if (e == hipSuccess) e = mark(2);
 
     // GEMM2, row-parallel with the shard sum in the accumulator:
-    // Y = H[:, 0:nh] . B^T[:, n_lo:n_lo+nh]^T (+ residual)
+    // Y = H[:, 0:nh] . B^T[:, n_lo:n_lo+nh]^T (+ residual), or, with the
+    // LayerNorm after, Z = residual + Y kept in fp32 for the Norm
+    float* Z = ln_after ? reinterpret_cast<float*>(wsb + L.z_off) : nullptr;
     if (e == hipSuccess) {
         GemmArgs g2;
         g2.A = H; g2.lda = nh;
         g2.B = bt + (size_t)n_lo * eb; g2.ldb = F;
         g2.M = M; g2.N = D; g2.K = nh;
-        g2.C = Y; g2.ldc = D; g2.c_dtype = y_dtype;
+        if (ln_after) {
+            g2.C = Z; g2.ldc = D; g2.c_dtype = TPMLP_F32;
+        } else {
+            g2.C = Y; g2.ldc = D; g2.c_dtype = y_dtype;
+        }
         g2.R = o.residual; g2.ldr = D;
         g2.epi = kEpiStore;
         g2.ab_dtype = s->dtype;
@@ -341,6 +353,8 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
         g2.split_ws_bytes = L.split_bytes;
         e = launch_gemm(g2, hs);
     }
+    // out = LayerNorm(Z), one rounding to Y's dtype
+    if (e == hipSuccess && ln_after) e = launch_ln_apply(Z, M, D, eps, Y, y_dtype, hs);
     if (e == hipSuccess) e = mark(3);
     return from_hip(e);
 }

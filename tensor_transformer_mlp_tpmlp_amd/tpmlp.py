@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libtpmlp.so")
 
 F32, BF16 = 0, 1
 OPT_LAYERNORM = 1
+OPT_LAYERNORM_AFTER = 2
 STATUS_NAMES = {
     0: "TPMLP_OK", 1: "TPMLP_ERR_NULL", 2: "TPMLP_ERR_SHAPE", 3: "TPMLP_ERR_INDIVISIBLE",
     4: "TPMLP_ERR_DTYPE", 5: "TPMLP_ERR_WORKSPACE", 6: "TPMLP_ERR_ALIGN", 7: "TPMLP_ERR_HIP",
@@ -195,14 +196,16 @@ def shard_mlp(A: torch.Tensor, B: torch.Tensor, n: int) -> Shards:
     return Shards(h.value, packed, D, F, n, A.dtype)
 
 
-def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, eps: float = 1e-5,
+def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, layernorm_after: bool = False,
+           eps: float = 1e-5,
            residual: Optional[torch.Tensor] = None, shard_index: int = -1,
            out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
            events: Optional[Sequence[int]] = None,
            save_preact: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = sum_i GeLU(X A_i) B_i on the GPU (tpmlp_forward_ex).
 
-    layernorm: normalise each row of X first (no affine); residual: added once
+    layernorm: normalise each row of X first (no affine); layernorm_after:
+    normalise each row of residual + Y last instead; residual: added once
     after the shard sum; shard_index: return only partial Y_i; events: four
     hipEvent_t handles recorded around the kernels (timing hook);
     save_preact: an (M, F) tensor (F/n with shard_index) of the weights'
@@ -218,7 +221,7 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, eps: flo
         out = torch.empty((M, shards.D), dtype=y_dtype, device=X.device)
     elif out.dtype != y_dtype or tuple(out.shape) != (M, shards.D):
         raise ValueError("out has the wrong dtype or shape")
-    flags = OPT_LAYERNORM if layernorm else 0
+    flags = (OPT_LAYERNORM if layernorm else 0) | (OPT_LAYERNORM_AFTER if layernorm_after else 0)
     L = lib()
     nbytes = L.tpmlp_forward_workspace_bytes(shards.handle, M, flags, 1 if shard_index >= 0 else 0)
     ws = shards.workspace(nbytes)

@@ -51,10 +51,15 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str) -> flo
 
 
 def oracle_forward(X: np.ndarray, A: np.ndarray, B: np.ndarray, n: int, layernorm: bool = False,
-                   residual: bool = False, eps: float = oracle.LN_EPS) -> np.ndarray:
+                   residual: bool = False, eps: float = oracle.LN_EPS,
+                   layernorm_after: bool = False) -> np.ndarray:
     """fp64 oracle of what tp_mlp computes with the given options."""
     shards = oracle.shard_mlp(A, B, n)
     x = X.astype(np.float64)
+    if layernorm_after:
+        if residual:
+            return oracle.norm_after_ffn(x, shards, eps)
+        return oracle.layer_norm(oracle.tp_mlp(x, shards), eps)
     xin = oracle.layer_norm(x, eps) if layernorm else x
     Y = oracle.tp_mlp(xin, shards)
     return x + Y if residual else Y

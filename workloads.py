@@ -18,7 +18,9 @@ The shapes follow the workloads of the pages (tokens M = b*s rows of width D,
 A of shape (D, F), B of shape (F, D), N shards): the worked example of
 "Tensor-Parallel MLP (Megatron)" (section "The split", "Example"), a small
 fp32 case, three bf16 sizes, and the FFN half of the Post-LN block of
-"LLM Lab Notes 06" at s in {128, 256, 512}.
+"LLM Lab Notes 06" at s in {128, 256, 512}, with the LayerNorm before the
+MLP as that page's code places it and after the residual as its prose does
+(the same inputs for both).
 """
 
 from __future__ import annotations
@@ -50,6 +52,7 @@ class Workload:
     layernorm: bool = False
     residual: bool = False
     note: str = ""
+    layernorm_after: bool = False
 
     @property
     def flops(self) -> int:
@@ -72,6 +75,12 @@ for _s in (128, 256, 512):
         f"postln_s{_s}_bf16", 8 * _s, 1024, 4096, 4, "bf16", 1.0, 0.02, 0.02, 1005 + _s,
         layernorm=True, residual=True,
         note=f"Post-LN FFN half: LayerNorm -> TP-MLP -> x + Y, b=8, s={_s}, h=1024")
+    # the same inputs with the Norm moved after the residual (the order the
+    # prose of that page describes): LayerNorm(x + TP-MLP(x))
+    WORKLOADS[f"lnafter_s{_s}_bf16"] = Workload(
+        f"lnafter_s{_s}_bf16", 8 * _s, 1024, 4096, 4, "bf16", 1.0, 0.02, 0.02, 1005 + _s,
+        residual=True, layernorm_after=True,
+        note=f"FFN half, Norm after the residual: LayerNorm(x + TP-MLP(x)), b=8, s={_s}, h=1024")
 
 HEADLINE = "mlp_h4096_bf16"
 
