@@ -70,6 +70,10 @@ template <int WB> struct Tile {
     static constexpr int LPU = M / 32;            // direct loads per wave per unit
 };
 
+// The GeLU epilogue that also stores the pre-activation (GemmArgs::preact_out
+// set): its own instantiation, so the plain GeLU epilogue carries none of it.
+constexpr int kEpiGeluSave = 3;
+
 struct FastParams {
     const bf16* A;
     int64_t lda;
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // The epilogue's operand (the pre-activation, or the residual) is read
     // for the whole wave tile before the first row block is transformed, so
     // its memory latency is paid once rather than once per row block.
-    constexpr bool kHasAux = EPI != kEpiGelu;
+    constexpr bool kHasAux = EPI == kEpiGeluGrad || EPI == kEpiStore;
     bf16x4 ex[kHasAux ? NB : 1][kHasAux ? NB : 1];
     if constexpr (EPI == kEpiGeluGrad) {
 #pragma unroll
@@ -398,8 +402,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
                 for (int r = 0; r < 4; ++r) v[j][r] = __builtin_fmaf(rs, v[j][r], -rm * cs[r]);
             }
         }
-        if constexpr (EPI == kEpiGelu) {
-            if (p.preact) {
+        if constexpr (EPI == kEpiGelu || EPI == kEpiGeluSave) {
+            if constexpr (EPI == kEpiGeluSave) {
                 // the pre-activation, kept for a backward pass
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
@@ -587,7 +591,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 
 template <int WB>
 static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
-    if (g.epi == kEpiGelu) return launch_typed<WB, kEpiGelu, bf16>(g, 1, stream);
+    if (g.epi == kEpiGelu)
+        return g.preact_out ? launch_typed<WB, kEpiGeluSave, bf16>(g, 1, stream)
+                            : launch_typed<WB, kEpiGelu, bf16>(g, 1, stream);
     if (g.epi == kEpiGeluGrad) return launch_typed<WB, kEpiGeluGrad, bf16>(g, 1, stream);
     const int s = split_count(g, WB);
     if (s > 1) {
