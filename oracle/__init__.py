@@ -1,5 +1,7 @@
 """fp64 CPU oracle (test infrastructure only; never on the product path)."""
 
+from . import attention_oracle  # noqa: F401
+
 from .tpmlp_oracle import (  # noqa: F401
     GELU_CUBIC,
     LN_EPS,
