@@ -252,6 +252,79 @@ size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M);
 tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpmlp_shards* s, const void* preact,
                             void* dX, void* dA, void* dB, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The attention half of the block (head-sharded self-attention).
+ *
+ * "LLM Lab Notes 06: Building a Megatron-Style Transformer Block from
+ * Scratch", section 2, markers 2 to 4, with the attention of "Tensor
+ * Parallelism in Megatron", section 4: for every sequence of `seq` tokens
+ * and every head j (H heads of width d = h / H, rank i of p owning heads
+ * i H/p .. (i+1) H/p - 1),
+ *     x_n = LayerNorm(x)                                 (optional)
+ *     Q_j = x_n W^Q[:, j], K_j = x_n W^K[:, j], V_j = x_n W^V[:, j]
+ *     O_j = softmax(Q_j K_j^T / sqrt(d)) V_j             (no mask)
+ *     attn = [O_0 | ... | O_{H-1}]       (all_gather and cat of the ranks)
+ *       or   attn = sum_i O_(rank i) W^O_i (row-parallel output projection)
+ *     out = x + attn                                     (optional)
+ * W^Q[:, j] are columns j d .. (j+1) d - 1, W^O_i the rows of W^O for rank
+ * i's heads.  Attention runs over the tokens of each sequence, per head.
+ * bf16 only; d must be 64.
+ * ------------------------------------------------------------------------ */
+
+typedef struct tpmlp_attn tpmlp_attn;   /* opaque: packed attention weights */
+
+enum {
+    TPMLP_ATTN_LAYERNORM = 1,   /* normalise each row of x first (no affine)       */
+    TPMLP_ATTN_RESIDUAL = 2     /* add x to the result                             */
+};
+
+/* Bytes of the packed buffer for hidden size h (W^Q, W^K, W^V stacked and
+ * transposed, their column sums, and W^O transposed when with_out_proj).
+ * Returns 0 for invalid arguments (see tpmlp_attn_pack). */
+size_t tpmlp_attn_pack_bytes(int64_t hidden, int heads, int p, int dtype, int with_out_proj);
+
+/*
+ * tpmlp_attn_pack -- pack the projection weights for tpmlp_attention.
+ *   Wq, Wk, Wv  device, h x h row-major (x W), bf16; read only.
+ *   Wo          device, h x h row-major, or NULL for the concatenation
+ *               form (no output projection).
+ *   hidden      h = heads * 64; heads > 0; p > 0 divides heads.
+ *   packed      device, tpmlp_attn_pack_bytes(...) bytes, caller-owned,
+ *               must stay valid while the descriptor is used.
+ *   out         receives a host descriptor (free with tpmlp_attn_destroy);
+ *               set to NULL on error.
+ * Errors: TPMLP_ERR_NULL, TPMLP_ERR_SHAPE (h != 64 heads, sizes out of
+ * range), TPMLP_ERR_INDIVISIBLE (p does not divide heads), TPMLP_ERR_DTYPE
+ * (not bf16), TPMLP_ERR_WORKSPACE (packed too small), TPMLP_ERR_ALIGN,
+ * TPMLP_ERR_HIP.
+ */
+tpmlp_status tpmlp_attn_pack(const void* Wq, const void* Wk, const void* Wv, const void* Wo, int64_t hidden,
+                             int heads, int p, int dtype, void* packed, size_t packed_bytes, tpmlp_attn** out,
+                             void* stream);
+
+/* Frees the host descriptor only. */
+void tpmlp_attn_destroy(tpmlp_attn* a);
+
+/* Bytes of device workspace tpmlp_attention needs for batch x seq tokens:
+ * the LayerNorm statistics, Q|K|V (batch seq x 3h), V transposed (h x
+ * batch seq), the heads' outputs (batch seq x h) when W^O is packed, and
+ * the projection GEMMs' split-K scratch.  0 for invalid arguments. */
+size_t tpmlp_attn_workspace_bytes(const tpmlp_attn* a, int64_t batch, int64_t seq);
+
+/*
+ * tpmlp_attention -- the attention half described above.
+ *   x      device, (batch seq) x h row-major bf16, sequence b in rows
+ *          b seq .. (b+1) seq - 1.
+ *   out    device, (batch seq) x h bf16; must not overlap x or the workspace.
+ *   flags  TPMLP_ATTN_LAYERNORM | TPMLP_ATTN_RESIDUAL, or 0.
+ *   ln_eps LayerNorm epsilon; 0 selects 1e-5.
+ * batch = 0 or seq = 0 is a no-op.  Errors: TPMLP_ERR_NULL, TPMLP_ERR_SHAPE
+ * (negative sizes, batch > 65535, batch seq > 2^21, unknown flags), TPMLP_ERR_ALIGN,
+ * TPMLP_ERR_WORKSPACE, TPMLP_ERR_HIP; all but the last before any HIP call.
+ */
+tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tpmlp_attn* a, void* out, int flags,
+                             float ln_eps, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

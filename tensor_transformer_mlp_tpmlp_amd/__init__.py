@@ -6,6 +6,9 @@ ctypes binding.
 """
 
 from .tpmlp import (  # noqa: F401
+    ATTN_LAYERNORM,
+    ATTN_RESIDUAL,
+    AttnWeights,
     BF16,
     F32,
     LIB_PATH,
@@ -13,8 +16,10 @@ from .tpmlp import (  # noqa: F401
     OPT_LAYERNORM_AFTER,
     Shards,
     TpmlpError,
+    attention,
     gelu,
     lib,
+    shard_attention,
     shard_mlp,
     tp_mlp,
     tp_mlp_backward,

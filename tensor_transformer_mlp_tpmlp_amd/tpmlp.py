@@ -23,6 +23,8 @@ LIB_PATH = os.path.join(_PKG_DIR, "libtpmlp.so")
 F32, BF16 = 0, 1
 OPT_LAYERNORM = 1
 OPT_LAYERNORM_AFTER = 2
+ATTN_LAYERNORM = 1
+ATTN_RESIDUAL = 2
 STATUS_NAMES = {
     0: "TPMLP_OK", 1: "TPMLP_ERR_NULL", 2: "TPMLP_ERR_SHAPE", 3: "TPMLP_ERR_INDIVISIBLE",
     4: "TPMLP_ERR_DTYPE", 5: "TPMLP_ERR_WORKSPACE", 6: "TPMLP_ERR_ALIGN", 7: "TPMLP_ERR_HIP",
@@ -59,6 +61,13 @@ SIGNATURES = {
     "tpmlp_forward_ex": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, ctypes.POINTER(Opts), _c_vp]),
     "tpmlp_backward_workspace_bytes": (_c_sz, [_c_vp, _c_i64]),
     "tpmlp_backward": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "tpmlp_attn_pack_bytes": (_c_sz, [_c_i64, _c_int, _c_int, _c_int, _c_int]),
+    "tpmlp_attn_pack": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_sz,
+                                 ctypes.POINTER(_c_vp), _c_vp]),
+    "tpmlp_attn_destroy": (None, [_c_vp]),
+    "tpmlp_attn_workspace_bytes": (_c_sz, [_c_vp, _c_i64, _c_i64]),
+    "tpmlp_attention": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, ctypes.c_float, _c_vp, _c_sz,
+                                 _c_vp]),
 }
 
 _lib = None
@@ -289,3 +298,80 @@ def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards, out=None,
                             shards.handle, pp, _dev(dX, "dX") if M else dX.data_ptr(), _dev(dA, "dA"),
                             _dev(dB, "dB"), ws.data_ptr(), ws.numel(), _stream(X.device)), "tpmlp_backward")
     return dX, dA, dB
+
+
+class AttnWeights:
+    """Packed projection weights of the attention half (a tpmlp_attn descriptor).
+
+    Holds the packed buffer (owned here, as a torch tensor) and a grow-only
+    workspace.
+    """
+
+    def __init__(self, handle: int, packed: torch.Tensor, hidden: int, heads: int, p: int, has_wo: bool):
+        self._handle = handle
+        self.packed = packed
+        self.hidden, self.heads, self.p, self.has_wo = hidden, heads, p, has_wo
+        self.device = packed.device
+        self._ws: Optional[torch.Tensor] = None
+
+    @property
+    def handle(self) -> int:
+        return self._handle
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def close(self) -> None:
+        if self._handle:
+            lib().tpmlp_attn_destroy(self._handle)
+            self._handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def shard_attention(Wq: torch.Tensor, Wk: torch.Tensor, Wv: torch.Tensor, heads: int, p: int,
+                    Wo: Optional[torch.Tensor] = None) -> AttnWeights:
+    """Pack W^Q, W^K, W^V (h x h, x W) and optionally W^O for `heads` heads
+    over p ranks (tpmlp_attn_pack).  Without W^O the heads' outputs are
+    concatenated (all_gather + cat); with it, projected row-parallel."""
+    h = Wq.shape[0]
+    for name, W in (("Wq", Wq), ("Wk", Wk), ("Wv", Wv)) + ((("Wo", Wo),) if Wo is not None else ()):
+        if W.dim() != 2 or tuple(W.shape) != (h, h):
+            raise ValueError(f"{name} must be ({h}, {h})")
+        if W.dtype != Wq.dtype:
+            raise TypeError("the projection weights must share one dtype")
+    dt = _dtype_code(Wq.dtype)
+    L = lib()
+    nbytes = L.tpmlp_attn_pack_bytes(h, heads, p, dt, 1 if Wo is not None else 0)
+    packed = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=Wq.device)
+    hd = ctypes.c_void_p()
+    _check(L.tpmlp_attn_pack(_dev(Wq, "Wq"), _dev(Wk, "Wk"), _dev(Wv, "Wv"),
+                             _dev(Wo, "Wo") if Wo is not None else None, h, heads, p, dt, packed.data_ptr(),
+                             packed.numel(), ctypes.byref(hd), _stream(Wq.device)), "tpmlp_attn_pack")
+    return AttnWeights(hd.value, packed, h, heads, p, Wo is not None)
+
+
+def attention(x: torch.Tensor, batch: int, seq: int, weights: AttnWeights, *, layernorm: bool = True,
+              residual: bool = True, eps: float = 1e-5, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The attention half on the GPU (tpmlp_attention): x is (batch*seq, h),
+    sequence b in rows b*seq .. (b+1)*seq-1."""
+    if x.dim() != 2 or x.shape[1] != weights.hidden or x.shape[0] != batch * seq:
+        raise ValueError(f"x must be ({batch * seq}, {weights.hidden})")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.dtype != x.dtype or out.shape != x.shape:
+        raise ValueError("out must match x")
+    L = lib()
+    ws = weights.workspace(L.tpmlp_attn_workspace_bytes(weights.handle, batch, seq))
+    flags = (ATTN_LAYERNORM if layernorm else 0) | (ATTN_RESIDUAL if residual else 0)
+    M = batch * seq
+    _check(L.tpmlp_attention(_dev(x, "x") if M else x.data_ptr(), batch, seq, weights.handle,
+                             _dev(out, "out") if M else out.data_ptr(), flags, eps, ws.data_ptr(), ws.numel(),
+                             _stream(x.device)), "tpmlp_attention")
+    return out

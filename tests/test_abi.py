@@ -129,3 +129,33 @@ def test_binding_refuses_cpu_tensors():
         tp.gelu(torch.zeros(8))
     with pytest.raises(ValueError):
         tp.shard_mlp(torch.zeros(2, 4), torch.zeros(4, 2), 2)
+
+
+def test_attention_pack_validation(L):
+    mib = 1 << 20
+    assert L.tpmlp_attn_pack_bytes(1024, 16, 4, 1, 0) == 6 * mib + 12288
+    assert L.tpmlp_attn_pack_bytes(1024, 16, 4, 1, 1) == 8 * mib + 12288
+    assert L.tpmlp_attn_pack_bytes(64, 1, 1, 1, 0) == 3 * 64 * 64 * 2 + 768
+    for bad in [(1024, 16, 4, 0, 0), (1000, 16, 4, 1, 0), (1024, 16, 3, 1, 0), (1024, 16, 0, 1, 0),
+                (1024, 0, 1, 1, 0), (128, 1, 1, 1, 0)]:
+        assert L.tpmlp_attn_pack_bytes(*bad) == 0, bad
+
+    def pack(Wq=FAKE, Wo=None, h=128, heads=2, p=2, dt=1, packed=FAKE2, nbytes=1 << 20):
+        out = ctypes.c_void_p(0xDEAD)
+        st = L.tpmlp_attn_pack(Wq, FAKE, FAKE, Wo, h, heads, p, dt, packed, nbytes, ctypes.byref(out), None)
+        assert out.value is None  # cleared on error
+        return st
+
+    assert pack(dt=0) == DTYPE
+    assert pack(h=100) == SHAPE
+    assert pack(heads=0) == SHAPE
+    assert pack(p=3, heads=2) == INDIV
+    assert pack(Wq=None) == NULL
+    assert pack(packed=None) == NULL
+    assert pack(nbytes=1000) == WS
+    assert pack(Wq=FAKE + 8) == ALIGN
+    assert pack(Wo=FAKE + 4) == ALIGN
+    assert L.tpmlp_attn_pack(FAKE, FAKE, FAKE, None, 128, 2, 2, 1, FAKE2, 1 << 20, None, None) == NULL
+    assert L.tpmlp_attn_workspace_bytes(None, 2, 8) == 0
+    assert L.tpmlp_attention(FAKE, 2, 8, None, FAKE, 0, 0.0, FAKE, 1 << 20, None) == NULL
+    L.tpmlp_attn_destroy(None)

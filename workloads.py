@@ -137,3 +137,63 @@ def random_case(M: int, D: int, F: int, seed: int, dtype: str = "f32",
     sb = (1.0 / np.sqrt(F)) if sb is None else sb
     return Inputs(_draw(rng, (M, D), sx, dtype), _draw(rng, (D, F), sa, dtype),
                   _draw(rng, (F, D), sb, dtype))
+
+
+# ---------------------------------------------------------------------------
+# the attention half of the block
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    batch: int
+    seq: int
+    hidden: int
+    heads: int
+    p: int
+    sx: float
+    sw: float
+    seed: int
+    note: str = ""
+
+    @property
+    def M(self) -> int:
+        return self.batch * self.seq
+
+    @property
+    def flops(self) -> int:
+        """Projections 2*M*h*3h, scores and P V 2 * 2*b*s*s*h (every head), without W^O."""
+        return 2 * self.M * self.hidden * 3 * self.hidden + 4 * self.batch * self.seq * self.seq * self.hidden
+
+
+# The block of "LLM Lab Notes 06" (b = 8 as for its FFN, s in {128, 256, 512},
+# 4 ranks); the pages give no head count, so h = 1024 as 16 heads of 64.
+ATTN_WORKLOADS: Dict[str, AttnWorkload] = {}
+for _s in (128, 256, 512):
+    ATTN_WORKLOADS[f"attn_s{_s}_bf16"] = AttnWorkload(
+        f"attn_s{_s}_bf16", 8, _s, 1024, 16, 4, 1.0, 0.02, 2005 + _s,
+        note=f"attention half: LayerNorm -> QKV -> softmax(QK^T/8)V per head -> cat -> x + attn, b=8, s={_s}")
+
+
+@dataclass
+class AttnInputs:
+    x: np.ndarray
+    Wq: np.ndarray
+    Wk: np.ndarray
+    Wv: np.ndarray
+    Wo: np.ndarray
+
+
+def make_attn_inputs(w: AttnWorkload) -> AttnInputs:
+    """Seeded x[M,h], then W^Q, W^K, W^V, W^O [h,h] (bf16 values in float32 arrays)."""
+    return attn_case(w.batch, w.seq, w.hidden, w.seed, w.sx, w.sw)
+
+
+def attn_case(batch: int, seq: int, hidden: int, seed: int, sx: float = 1.0,
+              sw: Optional[float] = None) -> AttnInputs:
+    """Seeded attention inputs of any shape; sw defaults to 1/sqrt(h)."""
+    rng = np.random.default_rng(seed)
+    sw = (1.0 / np.sqrt(hidden)) if sw is None else sw
+    x = _draw(rng, (batch * seq, hidden), sx, "bf16")
+    W = [_draw(rng, (hidden, hidden), sw, "bf16") for _ in range(4)]
+    return AttnInputs(x, *W)
