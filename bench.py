@@ -3,6 +3,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+NAME is a TP-MLP workload (default: the headline size), an attention
+workload (attn_s{128,256,512}_bf16: the attention half of the block) or
+block_s{128,256,512}_bf16 (the whole block with the time of each half).
+
 One step is one full forward of the hot path, Y = sum_i GeLU_tanh(X A_i) B_i
 (plus LayerNorm and the residual for the Post-LN workloads), over inputs
 already resident in HBM.  Weights are packed before timing (they are static).
@@ -313,6 +317,159 @@ def bench_backward(args, w, inp, X, shards, dtype, dev) -> int:
     return 0
 
 
+ATTN_METRIC = "attention half TFLOP/s (2·M·h·3h projection + 4·b·s²·h scores and P·V), 1 MI355X"
+BLOCK_METRIC = "block forward ms per step (attention half + FFN half), 1 MI355X"
+
+
+def _timed_segments(args, step, nev):
+    """Warm up, then time args.steps calls of step(events) with nev HIP events
+    per call; returns (ms per step, [per-interval mean ms])."""
+    import numpy as np
+    import torch
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    evs = [[hip.create() for _ in range(nev)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(evs[k])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    seg = [float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in evs])) for i in range(nev - 1)]
+    hip.close()
+    return ms, seg
+
+
+def _oracle_cores() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                       default=os.cpu_count()))
+    except Exception:
+        return int(os.cpu_count() or 1)
+
+
+def bench_attention(args, w) -> int:
+    """The attention half (LayerNorm, QKV projection, per-head softmax
+    attention, heads concatenated, residual) on one attention workload."""
+    import numpy as np
+    import torch
+
+    import tensor_transformer_mlp_tpmlp_amd as tp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    inp = workloads.make_attn_inputs(w)
+    x, Wq, Wk, Wv = (torch.from_numpy(a).to(dev).to(torch.bfloat16).contiguous()
+                     for a in (inp.x, inp.Wq, inp.Wk, inp.Wv))
+    aw = tp.shard_attention(Wq, Wk, Wv, w.heads, w.p)
+    out = torch.empty_like(x)
+    torch.cuda.synchronize()
+
+    def step(ev):
+        tp.attention(x, w.batch, w.seq, aw, out=out, events=ev)
+
+    ms, (t_ln, t_proj, t_attn) = _timed_segments(args, step, 4)
+    log(f"[bench] {w.name}: {ms:.4f} ms/step (LN {t_ln:.4f}, projection {t_proj:.4f}, attention {t_attn:.4f})")
+    value = w.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    f_proj = 2.0 * w.M * w.hidden * 3 * w.hidden
+    f_attn = 4.0 * w.batch * w.seq * w.seq * w.hidden
+    kernel, t_k, f_k = ("attention", t_attn, f_attn) if t_attn >= t_proj else ("qkv_projection", t_proj, f_proj)
+    achieved = f_k / (t_k * 1e-3) / 1e12
+    res = {
+        "metric": ATTN_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "strong", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": w.hidden, "heads": w.heads,
+                   "p": w.p, "layernorm": True, "residual": True, "out_proj": False},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "kernels_ms": {"ln_stats": round(t_ln, 5), "qkv_projection": round(t_proj, 5),
+                       "attention": round(t_attn, 5)},
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import attention_oracle as ao
+        log("[bench] timing the fp64 oracle on the host")
+
+        def run(nb):
+            t0 = time.perf_counter()
+            ao.attention_half(inp.x[:nb * w.seq], inp.Wq, inp.Wk, inp.Wv, w.heads, w.p, nb, w.seq)
+            return time.perf_counter() - t0
+
+        run(1)
+        t1 = run(1)
+        nb = max(1, min(w.batch, int(args.cpu_seconds / max(t1, 1e-6))))
+        t = run(nb)
+        res["cpu_baseline"] = {
+            "value": w.flops * nb / w.batch / t / 1e12, "unit": "TFLOP/s", "cores": _oracle_cores(),
+            "kind": "oracle",
+            "sample": f"{'all' if nb == w.batch else 'first'} {nb} of {w.batch} sequences (independent), "
+                      f"s={w.seq}, h={w.hidden}, {w.heads} heads; numpy fp64 oracle, {t:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_block(args, s: int) -> int:
+    """The block forward of "LLM Lab Notes 06" (code order): x1 = x +
+    attn(LayerNorm(x)), out = x1 + TP-MLP(LayerNorm(x1)), with the time of
+    each half (the page's segment timing)."""
+    import torch
+
+    import tensor_transformer_mlp_tpmlp_amd as tp
+    import workloads
+
+    wa = workloads.ATTN_WORKLOADS[f"attn_s{s}_bf16"]
+    wf = workloads.WORKLOADS[f"postln_s{s}_bf16"]
+    dev = torch.device("cuda:0")
+    ai = workloads.make_attn_inputs(wa)
+    fi = workloads.make_inputs(wf)
+    bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16).contiguous()
+    x = bf(ai.x)
+    aw = tp.shard_attention(bf(ai.Wq), bf(ai.Wk), bf(ai.Wv), wa.heads, wa.p)
+    shards = tp.shard_mlp(bf(fi.A), bf(fi.B), wf.n)
+    x1, y = torch.empty_like(x), torch.empty_like(x)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def record(e):
+        if hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def step(ev):
+        if ev:
+            record(ev[0])
+        tp.attention(x, wa.batch, wa.seq, aw, out=x1)
+        if ev:
+            record(ev[1])
+        tp.tp_mlp(x1, shards, layernorm=True, residual=x1, out=y)
+        if ev:
+            record(ev[2])
+
+    ms, (t_attn, t_ffn) = _timed_segments(args, step, 3)
+    log(f"[bench] block s={s}: {ms:.4f} ms/step (attention {t_attn:.4f}, FFN {t_ffn:.4f})")
+    flops = wa.flops + wf.flops
+    res = {
+        "metric": BLOCK_METRIC, "value": round(ms, 5), "unit": "ms", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": False, "scaling": "strong", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"block_s{s}_bf16", "batch": wa.batch, "seq": s, "hidden": wa.hidden,
+                   "heads": wa.heads, "ffn": wf.F, "p": wa.p},
+        "segments_ms": {"attention": round(t_attn, 5), "ffn": round(t_ffn, 5)},
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,6 +507,10 @@ def main() -> int:
     import workloads
 
     name = args.workload or workloads.HEADLINE
+    if name in workloads.ATTN_WORKLOADS:
+        return bench_attention(args, workloads.ATTN_WORKLOADS[name])
+    if name.startswith("block_s"):
+        return bench_block(args, int(name[len("block_s"):].split("_")[0]))
     w = workloads.WORKLOADS[name]
     if args.copy_calibration:
         copy_calibration()

@@ -318,12 +318,16 @@ size_t tpmlp_attn_workspace_bytes(const tpmlp_attn* a, int64_t batch, int64_t se
  *   out    device, (batch seq) x h bf16; must not overlap x or the workspace.
  *   flags  TPMLP_ATTN_LAYERNORM | TPMLP_ATTN_RESIDUAL, or 0.
  *   ln_eps LayerNorm epsilon; 0 selects 1e-5.
+ *   events optional: 4 hipEvent_t recorded on the stream before the
+ *          LayerNorm statistics, before the QKV projection, before the
+ *          attention kernel and after the last kernel (NULL entries skipped).
  * batch = 0 or seq = 0 is a no-op.  Errors: TPMLP_ERR_NULL, TPMLP_ERR_SHAPE
  * (negative sizes, batch > 65535, batch seq > 2^21, unknown flags), TPMLP_ERR_ALIGN,
  * TPMLP_ERR_WORKSPACE, TPMLP_ERR_HIP; all but the last before any HIP call.
  */
 tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tpmlp_attn* a, void* out, int flags,
-                             float ln_eps, void* workspace, size_t workspace_bytes, void* stream);
+                             float ln_eps, void* workspace, size_t workspace_bytes, void* const* events,
+                             void* stream);
 
 #ifdef __cplusplus
 }

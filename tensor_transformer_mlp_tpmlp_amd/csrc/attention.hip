@@ -12,13 +12,13 @@
 // and-cat of "LLM Lab Notes 06", section 2, marker 3, optionally plus the
 // residual x (marker 4).
 //
-// One block of 256 threads (4 waves) owns 64 query rows of one (sequence,
-// head); wave w owns rows 16w .. 16w+15.  Keys and values stream through LDS
-// in tiles of 64 keys, double-buffered: the next tile's global loads are
-// issued before the current tile's products and written to the other buffer
-// after them.  Per tile a wave forms S (16 x 64) in 8 MFMAs, updates the
-// running row maximum and sum (online softmax in the log2 domain, fp32),
-// rounds P to bf16 and accumulates O (16 x 64) in 8 MFMAs.
+// One block of 256 threads (4 waves) owns 64 QB query rows of one (sequence,
+// head); wave w owns QB blocks of 16 rows, from row 16 QB w on.  Keys and
+// values stream through LDS in tiles of 64 keys.  Per tile a wave forms S
+// (16 QB x 64) in 8 QB MFMAs, updates the running row maximum and sum
+// (online softmax in the log2 domain, fp32), rounds P to bf16 and
+// accumulates O (16 QB x 64) in 8 QB MFMAs; each K and V^T fragment read
+// from LDS feeds QB of them.
 //
 // MFMA operand order: the first operand's rows index the result's rows as
 // seen by the lanes, so S = mfma(K frag, Q frag) leaves lane l with query
@@ -28,6 +28,8 @@
 // of the even 16-key block and {16 + 4g .. 16 + 4g + 3} of the odd one
 // (g = l >> 4); the V^T fragment is read with the same key order, which is
 // all the contraction needs.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -38,7 +40,6 @@ namespace {
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDH = 64;      // head width
-constexpr int kQT = 64;      // query rows per block
 constexpr int kKT = 64;      // keys per tile
 constexpr int kRowB = 128;   // bytes per LDS row (64 bf16)
 
@@ -60,6 +61,172 @@ struct AttnParams {
     float scale_log2;  // log2(e) / sqrt(d)
 };
 
+// One tile of 64 keys for one wave's QB blocks of 16 query rows: S = Q K^T,
+// the online softmax update, then O = alpha O + P V.  Every K and V^T
+// fragment read from LDS feeds QB MFMAs.  kb: the K tile (64 keys x 128
+// bytes), vb: the V^T tile (64 head columns x 128 bytes), both with the
+// chunk swizzle.
+//
+// Softmax bookkeeping per row (log2 domain, c = log2(e)/sqrt(d)):
+//   m_run: the reference maximum (in units of c s); P = 2^(c s - m_run);
+//   ls: the row sums of P, formed by an MFMA of P with a block of ones (so
+//       they sum exactly the bf16 P that multiplies V), scaled like O.
+// The reference maximum is raised only when a score of the tile exceeds it
+// by more than kLazy (then O and ls are rescaled by 2^(m_old - m_new));
+// otherwise P stays below 2^kLazy and nothing is rescaled.  O / ls is the
+// same for any reference at or below the true maximum, so this changes only
+// where the bf16 rounding of P falls.  The decision is taken per wave, so a
+// wave either rescales all its rows (each with its own factor) or none.
+constexpr float kLazy = 8.0f;
+
+template <int QB>
+__device__ __forceinline__ void attn_tile(const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb,
+                                          const bf16x8 (&qf)[QB][2], f32x4 (&o)[QB][4], f32x4 (&ls)[QB],
+                                          float (&m_run)[QB], int kv0, int seq, float c_log2, int g, int li) {
+    // S = Q K^T for the 64 keys of the tile: lane holds query li of block i, keys 16 jb + 4 g + r
+    f32x4 s[QB][4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        const int r = 16 * jb + li;
+#pragma unroll
+        for (int i = 0; i < QB; ++i) s[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            bf16x8 kf;
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(&kb[r * kRowB + (((4 * c + g) ^ swz(r)) << 4)]);
+            __builtin_memcpy(&kf, &raw, 16);
+#pragma unroll
+            for (int i = 0; i < QB; ++i)
+                s[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i][c], s[i][jb], 0, 0, 0);
+        }
+    }
+
+    // keys past the sequence end (only in a partial last tile) score -inf
+    if (kv0 + kKT > seq) {
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (kv0 + 16 * jb + 4 * g + r >= seq) s[i][jb][r] = -__builtin_inff();
+    }
+
+    float mc[QB];
+    bool raise = false;
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+        float mt = fmaxf(fmaxf(s[i][0][0], s[i][0][1]), fmaxf(s[i][0][2], s[i][0][3]));
+#pragma unroll
+        for (int jb = 1; jb < 4; ++jb)
+            mt = fmaxf(fmaxf(mt, fmaxf(s[i][jb][0], s[i][jb][1])), fmaxf(s[i][jb][2], s[i][jb][3]));
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mc[i] = mt * c_log2;
+        raise |= mc[i] > m_run[i] + kLazy;
+    }
+    if (__any(raise)) {
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+            const float m_new = fmaxf(m_run[i], mc[i]);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[i] - m_new);
+            m_run[i] = m_new;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[i][db] *= alpha;
+            ls[i] *= alpha;
+        }
+    }
+
+    // P = 2^(c s - m_run), rounded to bf16, in the k-slot order of the PV MFMA
+    bf16x8 pf[QB][2];
+#pragma unroll
+    for (int i = 0; i < QB; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pf[i][jb >> 1][4 * (jb & 1) + r] =
+                    static_cast<bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[i][jb][r], c_log2, -m_run[i])));
+
+    // row sums: P times a 32 x 16 block of ones, per 32-key chunk
+    bf16x8 ones;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ones[k] = static_cast<bf16>(1.0f);
+#pragma unroll
+    for (int i = 0; i < QB; ++i)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) ls[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[i][c], ls[i], 0, 0, 0);
+
+    // O += P V: V^T rows are head columns; keys in the P fragment's order
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int r = 16 * db + li;
+        const uint8_t* vrow = &vb[r * kRowB];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            // keys 32c + 4g .. +3 and 32c + 16 + 4g .. +3: 8-byte halves of 16-byte chunks
+            const int ch0 = 4 * c + (g >> 1), ch1 = 4 * c + 2 + (g >> 1);
+            const int half = (g & 1) << 3;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ((ch0 ^ swz(r)) << 4) + half);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ((ch1 ^ swz(r)) << 4) + half);
+            const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+            bf16x8 vf;
+            __builtin_memcpy(&vf, &raw, 16);
+#pragma unroll
+            for (int i = 0; i < QB; ++i)
+                o[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i][c], o[i][db], 0, 0, 0);
+        }
+    }
+}
+
+// Q fragments of a wave's QB row blocks (zeros past the sequence end):
+// lane l holds row 16 i + (l & 15) of the wave's rows, d = 32 c + 8 (l >> 4) ..
+template <int QB>
+__device__ __forceinline__ void load_q(const AttnParams& p, int64_t tok0, int qw, int g, int li,
+                                       bf16x8 (&qf)[QB][2], int head) {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+        const int q = qw + 16 * i + li;
+        const bf16* qrow = p.qkv + (tok0 + q) * p.ldq + head * kDH;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (q < p.seq) raw = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
+            __builtin_memcpy(&qf[i][c], &raw, 16);
+        }
+    }
+}
+
+// O / (row sum) for every row block, plus the residual, rounded to bf16; lane l
+// writes row 16 i + (l & 15), columns 16 db + 4 (l >> 4) .. +3.
+template <int QB>
+__device__ __forceinline__ void store_o(const AttnParams& p, int64_t tok0, int qw, int g, int li, int head,
+                                        f32x4 (&o)[QB][4], const f32x4 (&ls)[QB]) {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+        // every column of the ones product holds the row sum of this lane's row
+        const float inv = 1.0f / ls[i][0];
+        const int q = qw + 16 * i + li;
+        if (q >= p.seq) continue;
+        const int64_t row = tok0 + q;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const int64_t col = (int64_t)head * kDH + 16 * db + 4 * g;
+            f32x4 v = o[i][db] * inv;
+            if (p.x) {
+                const bf16x4 xr = *reinterpret_cast<const bf16x4*>(p.x + row * p.ldx + col);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] += static_cast<float>(xr[r]);
+            }
+            bf16x4 ov;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ov[r] = static_cast<bf16>(v[r]);
+            *reinterpret_cast<bf16x4*>(p.out + row * p.ldo + col) = ov;
+        }
+    }
+}
+
+template <int QB>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kKT * kRowB];
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][kDH * kRowB];
@@ -70,23 +237,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
     const int g = lane >> 4;
     const int li = lane & 15;
     const int seq = p.seq;
-    const int q0 = blockIdx.x * kQT;
+    const int qw = blockIdx.x * 64 * QB + 16 * QB * w;  // this wave's first query row
     const int head = blockIdx.y;
     const int64_t tok0 = (int64_t)blockIdx.z * seq;  // first token row of this sequence
     const bool vt_vec = (seq & 7) == 0;              // 16-byte V^T chunks stay in one sequence
 
-    // Q fragments of this lane's row (zeros past the sequence end)
-    bf16x8 qf[2];
-    {
-        const int q = q0 + 16 * w + li;
-        const bf16* qrow = p.qkv + (tok0 + q) * p.ldq + head * kDH;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (q < seq) raw = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
-            __builtin_memcpy(&qf[c], &raw, 16);
-        }
-    }
+    bf16x8 qf[QB][2];
+    load_q<QB>(p, tok0, qw, g, li, qf, head);
 
     // tile loader: thread t moves K chunks (row t/8, t/8+32; chunk t%8) and
     // V^T chunks (head column t/8, t/8+32; keys 8 (t%8) ..), 16 bytes each
@@ -123,11 +280,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
         }
     };
 
-    f32x4 o[4];
+    f32x4 o[QB][4], ls[QB];
+    float m_run[QB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -__builtin_inff();
-    float l_run = 0.f;
+    for (int i = 0; i < QB; ++i) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ls[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[i] = -__builtin_inff();
+    }
 
     const int ntiles = (seq + kKT - 1) / kKT;
     load_tile(0);
@@ -137,96 +298,102 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
         const int b = it & 1;
         const int kv0 = it * kKT;
         if (it + 1 < ntiles) load_tile(kv0 + kKT);
-
-        // S = Q K^T for the 64 keys of the tile: lane holds query li, keys 16 jb + 4 g + r
-        f32x4 s[4];
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            s[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int r = 16 * jb + li;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                bf16x8 kf;
-                const u32x4 raw = *reinterpret_cast<const u32x4*>(&kbuf[b][r * kRowB + (((4 * c + g) ^ swz(r)) << 4)]);
-                __builtin_memcpy(&kf, &raw, 16);
-                s[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], s[jb], 0, 0, 0);
-            }
-        }
-
-        // online softmax in the log2 domain; keys past the sequence end are -inf
-        float mt = -__builtin_inff();
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int kv = kv0 + 16 * jb + 4 * g + r;
-                const float v = kv < seq ? s[jb][r] * p.scale_log2 : -__builtin_inff();
-                s[jb][r] = v;
-                mt = fmaxf(mt, v);
-            }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float lsum = 0.f;
-        bf16x8 pf[2];
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bf16 pb = static_cast<bf16>(__builtin_amdgcn_exp2f(s[jb][r] - m_new));
-                lsum += static_cast<float>(pb);
-                pf[jb >> 1][4 * (jb & 1) + r] = pb;
-            }
-        l_run = __builtin_fmaf(l_run, alpha, lsum);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-
-        // O += P V: V^T rows are head columns; keys in the P fragment's order
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int r = 16 * db + li;
-            const uint8_t* vrow = &vbuf[b][r * kRowB];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                // keys 32c + 4g .. +3 and 32c + 16 + 4g .. +3: 8-byte halves of 16-byte chunks
-                const int ch0 = 4 * c + (g >> 1), ch1 = 4 * c + 2 + (g >> 1);
-                const int half = (g & 1) << 3;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ((ch0 ^ swz(r)) << 4) + half);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ((ch1 ^ swz(r)) << 4) + half);
-                const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
-                bf16x8 vf;
-                __builtin_memcpy(&vf, &raw, 16);
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[c], o[db], 0, 0, 0);
-            }
-        }
-
+        attn_tile<QB>(kbuf[b], vbuf[b], qf, o, ls, m_run, kv0, seq, p.scale_log2, g, li);
         if (it + 1 < ntiles) store_tile(b ^ 1);
         __syncthreads();
     }
+    store_o<QB>(p, tok0, qw, g, li, head, o, ls);
+}
 
-    // the row sum over the four lanes that share a query row, then O / l
-    float l = l_run + __shfl_xor(l_run, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = 1.0f / l;
-    const int q = q0 + 16 * w + li;
-    if (q >= seq) return;
-    const int64_t row = tok0 + q;
+// s_waitcnt immediates (gfx9): vmcnt in bits [3:0] and [15:14], expcnt and
+// lgkmcnt left at their maxima (no wait) unless asked for.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kStages = 3;
+constexpr int kTileB = kKT * kRowB;  // 8 KiB: one K tile or one V^T tile
+
+// The same computation with the key and value tiles moved by direct
+// global-to-LDS loads (16 bytes per lane) through a ring of three stages, so
+// each tile's loads are issued two tiles ahead of its use and no registers
+// stage them.  Wave w fills LDS rows 16 w .. 16 w + 15 of each tile in two
+// loads of 8 rows; lane L lands at row 16 w + 8 q + L/8, physical chunk L % 8,
+// so it reads the logical chunk (L % 8) ^ swz(row) of that row.  Buffer
+// resources bound every read to the end of QKV and V^T: rows past the last
+// sequence read as zero, and keys of the next sequence are masked like any
+// key past the sequence end.  Requires seq % 8 == 0 (16-byte aligned V^T
+// chunks) and both buffers below 2 GiB.
+template <int QB>
+__global__ __launch_bounds__(256) void attn_fwd_ring_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][2][kTileB];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int g = lane >> 4;
+    const int li = lane & 15;
+    const int seq = p.seq;
+    const int qw = blockIdx.x * 64 * QB + 16 * QB * w;
+    const int head = blockIdx.y;
+    const int64_t tok0 = (int64_t)blockIdx.z * seq;
+    const int64_t M = p.ldv;
+
+    bf16x8 qf[QB][2];
+    load_q<QB>(p, tok0, qw, g, li, qf, head);
+
+    const int64_t k_off = tok0 * p.ldq + p.h + (int64_t)head * kDH;
+    const int64_t v_off = (int64_t)head * kDH * p.ldv + tok0;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>(p.qkv + k_off), (short)0, (int)((M * p.ldq - k_off) * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>(p.vt + v_off), (short)0, (int)((p.h * p.ldv - v_off) * 2), 0x00020000);
+    const int r0 = 16 * w + (lane >> 3);
+    const int r1 = r0 + 8;
+    const int pc = lane & 7;
+    const uint32_t kv_0 = (uint32_t)(r0 * p.ldq * 2 + ((pc ^ swz(r0)) << 4));
+    const uint32_t kv_1 = (uint32_t)(r1 * p.ldq * 2 + ((pc ^ swz(r1)) << 4));
+    const uint32_t vv_0 = (uint32_t)(r0 * p.ldv * 2 + ((pc ^ swz(r0)) << 4));
+    const uint32_t vv_1 = (uint32_t)(r1 * p.ldv * 2 + ((pc ^ swz(r1)) << 4));
+    const int dst0 = 16 * w * kRowB, dst1 = dst0 + 8 * kRowB;
+
+    auto issue = [&](int kv0, int st) {
+        const uint32_t ks = (uint32_t)(kv0 * p.ldq * 2), vs = (uint32_t)(kv0 * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(&ring[st][0][dst0]), 16, kv_0, ks, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(&ring[st][0][dst1]), 16, kv_1, ks, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(&ring[st][1][dst0]), 16, vv_0, vs, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(&ring[st][1][dst1]), 16, vv_1, vs, 0, 0);
+    };
+
+    f32x4 o[QB][4], ls[QB];
+    float m_run[QB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        const int64_t col = (int64_t)head * kDH + 16 * db + 4 * g;
-        f32x4 v = o[db] * inv;
-        if (p.x) {
-            const bf16x4 xr = *reinterpret_cast<const bf16x4*>(p.x + row * p.ldx + col);
+    for (int i = 0; i < QB; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] += static_cast<float>(xr[r]);
-        }
-        bf16x4 ov;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ov[r] = static_cast<bf16>(v[r]);
-        *reinterpret_cast<bf16x4*>(p.out + row * p.ldo + col) = ov;
+        for (int db = 0; db < 4; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ls[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[i] = -__builtin_inff();
     }
+
+    const int ntiles = (seq + kKT - 1) / kKT;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the Q fragments
+    issue(0, 0);
+    if (ntiles > 1) issue(kKT, 1);
+    int st = 0;
+    for (int it = 0; it < ntiles; ++it) {
+        // this tile's four loads have landed (the next tile's may be in flight),
+        // and every wave is done reading the stage the next issue overwrites
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+        if (it + 1 < ntiles)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_barrier();
+        if (it + 2 < ntiles) issue((it + 2) * kKT, st == 0 ? 2 : st - 1);
+        attn_tile<QB>(ring[st][0], ring[st][1], qf, o, ls, m_run, it * kKT, seq, p.scale_log2, g, li);
+        st = st == 2 ? 0 : st + 1;
+    }
+    store_o<QB>(p, tok0, qw, g, li, head, o, ls);
 }
 
 }  // namespace
@@ -246,8 +413,22 @@ hipError_t launch_attention(const void* qkv, int64_t ldq, const void* vt, int64_
     p.h = heads * kDH;
     p.seq = (int)seq;
     p.scale_log2 = (float)(kLog2e / 8.0);  // 1 / sqrt(64) = 1/8
-    const dim3 grid((unsigned)((seq + kQT - 1) / kQT), (unsigned)heads, (unsigned)batch);
-    attn_fwd_kernel<<<grid, dim3(256), 0, stream>>>(p);
+    const int64_t M = batch * seq;
+    const bool ring = seq % 8 == 0 && M * ldq * 2 < ((int64_t)1 << 31) && p.h * ldv * 2 < ((int64_t)1 << 31);
+    // 64 query rows per wave for long sequences (each K/V fragment feeds four
+    // MFMAs); 32 otherwise, which keeps more blocks for short ones
+    auto launch = [&](auto qb) {
+        constexpr int QB = decltype(qb)::value;
+        const dim3 grid((unsigned)((seq + 64 * QB - 1) / (64 * QB)), (unsigned)heads, (unsigned)batch);
+        if (ring)
+            attn_fwd_ring_kernel<QB><<<grid, dim3(256), 0, stream>>>(p);
+        else
+            attn_fwd_kernel<QB><<<grid, dim3(256), 0, stream>>>(p);
+    };
+    if (seq >= 1024)
+        launch(std::integral_constant<int, 4>{});
+    else
+        launch(std::integral_constant<int, 2>{});
     return hipGetLastError();
 }
 

@@ -155,7 +155,8 @@ size_t tpmlp_attn_workspace_bytes(const tpmlp_attn* a, int64_t batch, int64_t se
 }
 
 tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tpmlp_attn* a, void* out, int flags,
-                             float ln_eps, void* workspace, size_t workspace_bytes, void* stream) {
+                             float ln_eps, void* workspace, size_t workspace_bytes, void* const* events,
+                             void* stream) {
     if (!a) return TPMLP_ERR_NULL;
     if (batch < 0 || seq < 0 || seq > kMaxTokens || (seq > 0 && batch > kMaxTokens / seq)) return TPMLP_ERR_SHAPE;
     if (batch > kMaxBatch) return TPMLP_ERR_SHAPE;
@@ -182,8 +183,14 @@ tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tp
     char* qkv = w + L.qkv;
     char* vt = w + L.vt;
 
-    hipError_t e = hipSuccess;
-    if (ln) e = launch_ln_stats(x, M, h, kBF16, eps, mean, rstd, hs);
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (events)
+        for (int k = 0; k < 4; ++k) ev[k] = static_cast<hipEvent_t>(events[k]);
+    auto mark = [&](int k) -> hipError_t { return ev[k] ? hipEventRecord(ev[k], hs) : hipSuccess; };
+
+    hipError_t e = mark(0);
+    if (e == hipSuccess && ln) e = launch_ln_stats(x, M, h, kBF16, eps, mean, rstd, hs);
+    if (e == hipSuccess) e = mark(1);
     // [Q | K | V] = LayerNorm?(x) [Wq | Wk | Wv]: one GEMM for every head of every rank
     if (e == hipSuccess) {
         GemmArgs g = proj_shape(M, 3 * h, h);
@@ -199,6 +206,7 @@ tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tp
     }
     // V^T (h x M): the P V product contracts over keys
     if (e == hipSuccess) e = launch_transpose(qkv + (size_t)2 * h * 2, 3 * h, vt, M, M, h, 2, hs);
+    if (e == hipSuccess) e = mark(2);
     if (e == hipSuccess) {
         if (!a->has_wo) {
             // the heads' outputs side by side (all_gather + cat), plus x
@@ -220,6 +228,7 @@ tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tp
             }
         }
     }
+    if (e == hipSuccess) e = mark(3);
     return from_hip(e);
 }
 

@@ -67,7 +67,7 @@ SIGNATURES = {
     "tpmlp_attn_destroy": (None, [_c_vp]),
     "tpmlp_attn_workspace_bytes": (_c_sz, [_c_vp, _c_i64, _c_i64]),
     "tpmlp_attention": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, ctypes.c_float, _c_vp, _c_sz,
-                                 _c_vp]),
+                                 _c_vp, _c_vp]),
 }
 
 _lib = None
@@ -358,9 +358,11 @@ def shard_attention(Wq: torch.Tensor, Wk: torch.Tensor, Wv: torch.Tensor, heads:
 
 
 def attention(x: torch.Tensor, batch: int, seq: int, weights: AttnWeights, *, layernorm: bool = True,
-              residual: bool = True, eps: float = 1e-5, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+              residual: bool = True, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+              events: Optional[Sequence[int]] = None) -> torch.Tensor:
     """The attention half on the GPU (tpmlp_attention): x is (batch*seq, h),
-    sequence b in rows b*seq .. (b+1)*seq-1."""
+    sequence b in rows b*seq .. (b+1)*seq-1; events: four hipEvent_t handles
+    recorded around the kernels (timing hook)."""
     if x.dim() != 2 or x.shape[1] != weights.hidden or x.shape[0] != batch * seq:
         raise ValueError(f"x must be ({batch * seq}, {weights.hidden})")
     if out is None:
@@ -371,7 +373,11 @@ def attention(x: torch.Tensor, batch: int, seq: int, weights: AttnWeights, *, la
     ws = weights.workspace(L.tpmlp_attn_workspace_bytes(weights.handle, batch, seq))
     flags = (ATTN_LAYERNORM if layernorm else 0) | (ATTN_RESIDUAL if residual else 0)
     M = batch * seq
+    ev_arr = None
+    if events is not None:
+        ev_arr = (ctypes.c_void_p * 4)(*[e or None for e in events])
     _check(L.tpmlp_attention(_dev(x, "x") if M else x.data_ptr(), batch, seq, weights.handle,
                              _dev(out, "out") if M else out.data_ptr(), flags, eps, ws.data_ptr(), ws.numel(),
+                             ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
                              _stream(x.device)), "tpmlp_attention")
     return out

@@ -157,5 +157,5 @@ def test_attention_pack_validation(L):
     assert pack(Wo=FAKE + 4) == ALIGN
     assert L.tpmlp_attn_pack(FAKE, FAKE, FAKE, None, 128, 2, 2, 1, FAKE2, 1 << 20, None, None) == NULL
     assert L.tpmlp_attn_workspace_bytes(None, 2, 8) == 0
-    assert L.tpmlp_attention(FAKE, 2, 8, None, FAKE, 0, 0.0, FAKE, 1 << 20, None) == NULL
+    assert L.tpmlp_attention(FAKE, 2, 8, None, FAKE, 0, 0.0, FAKE, 1 << 20, None, None) == NULL
     L.tpmlp_attn_destroy(None)

@@ -56,8 +56,12 @@ ATTN_SHAPES = [
     (2, 5, 2, 2, 1.0),       # shorter than a tile, seq % 8 != 0
     (2, 64, 4, 2, 1.0),      # exactly one tile
     (3, 100, 4, 4, 1.0),     # two tiles, ragged, seq % 8 != 0
-    (2, 136, 2, 1, 1.0),     # three tiles, ragged, seq % 8 == 0
+    (2, 136, 2, 1, 1.0),     # three tiles, ragged, seq % 8 == 0 (LDS-ring kernel)
+    (3, 200, 2, 2, 1.0),     # four tiles, ragged, seq % 8 == 0 (LDS-ring kernel)
     (2, 300, 4, 2, 1.0),     # five tiles
+    (1, 512, 2, 1, 1.0),     # eight full tiles (LDS-ring kernel)
+    (1, 1024, 2, 2, 1.0),    # 64 query rows per wave (LDS-ring kernel)
+    (2, 1100, 1, 1, 1.0),    # 64 query rows per wave, ragged, seq % 8 != 0
 ]
 
 
@@ -71,7 +75,8 @@ def test_attention_shapes(batch, seq, heads, p, sws, with_wo):
     _check(inp, batch, seq, heads, p, with_wo, True, f"b={batch} s={seq} H={heads}")
 
 
-def test_attention_peaked_scores_exact_projections():
+@pytest.mark.parametrize("seq", [100, 136])
+def test_attention_peaked_scores_exact_projections(seq):
     """Scores with standard deviation about 11, where the softmax is nearly
     one-hot.  With real-valued inputs the bf16 storage of Q, K and V alone
     would move such a softmax by a few percent, so here x is drawn from
@@ -80,7 +85,7 @@ def test_attention_peaked_scores_exact_projections():
     in fp32 and in bf16, and so are the scores.  What remains is the
     kernel's own arithmetic (exp2, P rounded to bf16, fp32 sums), compared
     with the fp64 oracle at the usual bound."""
-    batch, seq, heads, p = 3, 100, 4, 4
+    batch, heads, p = 3, 4, 4
     h = 64 * heads
     say(f"peaked scores b={batch} s={seq} H={heads}, exact projections")
     rng = np.random.default_rng(77)
@@ -132,7 +137,7 @@ def test_attention_empty_and_errors():
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     call = lambda xp, b, s, flags, wsb: L.tpmlp_attention(xp, b, s, aw.handle, out.data_ptr(), flags, 0.0,
-                                                          ws.data_ptr(), wsb, None)
+                                                          ws.data_ptr(), wsb, None, None)
     assert call(x.data_ptr(), 0, 16, 3, nbytes) == 0      # nothing to do
     assert call(x.data_ptr(), 2, 0, 3, nbytes) == 0
     assert call(x.data_ptr(), -1, 16, 3, nbytes) == 2
