@@ -10,9 +10,10 @@ block_s{128,256,512}_bf16 (the whole block with the time of each half).
 One step is one full forward of the hot path, Y = sum_i GeLU_tanh(X A_i) B_i
 (plus LayerNorm and the residual for the Post-LN workloads), over inputs
 already resident in HBM.  Weights are packed before timing (they are static).
-Prints ONE JSON line: whole-forward TFLOP/s (4*M*D*F per step), the roofline
-of the dominant kernel from HIP events recorded around each kernel inside the
-timed loop, and the fp64 oracle timed on the host cores on a row sample.
+Prints ONE JSON line: whole-forward TFLOP/s (4*M*D*F per step, from a timed
+loop with no events inside it), the roofline of the dominant kernel from HIP
+events recorded around each kernel in a second pass of the same steps, and
+the fp64 oracle timed on the host cores on a row sample.
 """
 
 from __future__ import annotations
@@ -321,25 +322,32 @@ ATTN_METRIC = "attention half TFLOP/s (2·M·h·3h projection + 4·b·s²·h sco
 BLOCK_METRIC = "block forward ms per step (attention half + FFN half), 1 MI355X"
 
 
-def _timed_segments(args, step, nev):
-    """Warm up, then time args.steps calls of step(events) with nev HIP events
-    per call; returns (ms per step, [per-interval mean ms])."""
+def _timed_segments(args, step, nev, warm=True):
+    """Warm up, time args.steps calls of step(None) between two events on the
+    stream (the per-step time: nothing else is recorded inside the loop),
+    then run the same number of steps again with nev HIP events per call
+    around the kernels (each record costs a few microseconds of queue time,
+    which is why it stays out of the first loop).  Returns (ms per step,
+    [mean ms of each of the nev - 1 intervals])."""
     import numpy as np
     import torch
 
-    for _ in range(args.warmup):
-        step(None)
+    if warm:
+        for _ in range(args.warmup):
+            step(None)
     torch.cuda.synchronize()
-    hip = HipEvents()
-    evs = [[hip.create() for _ in range(nev)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
-    for k in range(args.steps):
-        step(evs[k])
+    for _ in range(args.steps):
+        step(None)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    hip = HipEvents()
+    evs = [[hip.create() for _ in range(nev)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
     seg = [float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in evs])) for i in range(nev - 1)]
     hip.close()
     return ms, seg
@@ -539,20 +547,8 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup steps done")
 
-    hip = HipEvents()
-    evs = [[hip.create() for _ in range(4)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for k in range(args.steps):
-        step(evs[k])
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    t_ln = [hip.elapsed_ms(e[0], e[1]) for e in evs]
-    t_g1 = [hip.elapsed_ms(e[1], e[2]) for e in evs]
-    t_g2 = [hip.elapsed_ms(e[2], e[3]) for e in evs]
-    hip.close()
+    ms, (t_ln, t_g1, t_g2) = _timed_segments(args, step, 4, warm=False)
+    t_ln, t_g1, t_g2 = [t_ln], [t_g1], [t_g2]
     log(f"[bench] {args.steps} timed steps: {ms:.4f} ms/step")
 
     flops = float(w.flops)
