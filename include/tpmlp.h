@@ -215,10 +215,10 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
                               const tpmlp_opts* opts, void* stream);
 
 /*
- * Bytes of device workspace tpmlp_backward needs for M rows: the weights
- * unpacked to A (D x F) and B (F x D), three M x F intermediates (S = X A
- * then dS^T, H^T = GeLU(S)^T, and dS), transposed copies of X and dY (D x M
- * each), all in the weights' dtype, plus the split-K scratch of its GEMMs.  Returns 0 for
+ * Bytes of device workspace tpmlp_backward needs for M rows: three M x F
+ * intermediates in the weights' dtype (S = X A, H = GeLU(S) and dS), plus
+ * the split-K scratch of its GEMMs.  No operand is copied or transposed:
+ * the GEMMs read X, dY, dS, H and the packed weights where they lie.  Returns 0 for
  * invalid arguments.
  */
 size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M);

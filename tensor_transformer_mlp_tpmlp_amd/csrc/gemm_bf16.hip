@@ -114,6 +114,29 @@ constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
 // which is conflict-free under any key.
 __device__ __forceinline__ uint32_t lds_key(uint32_t r) { return ((r & 8) >> 2) | ((r & 2) << 1); }
 
+// LDS layout of a K-major unit: row r (one k) of 2 BM bytes, its 16-byte
+// chunk c at physical chunk c ^ kswz(r), kswz(r) = 2 ((r & 3) + 4 ((r >> 3) & 1)).
+// Rows start on the same bank (their length is a multiple of 256 bytes); a
+// transposing fragment read takes 32 bytes from each of 16 rows 8 g + 4 h + i
+// (g = 0..3, i = 0..3), and the key gives the rows of each half-wave eight
+// distinct 32-byte bank groups.
+__device__ __forceinline__ uint32_t kswz(uint32_t r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane direct load into LDS at the wave-uniform address dst,
+// written out so that the compiler does not see an LDS write in flight: it
+// would otherwise wait for every such load before each transposing LDS read
+// (it cannot tell the ring slots apart).  The kernels order these loads
+// against their readers themselves (vmcnt waits and barriers).  M0 holds the
+// LDS address; the s_nop is the wait state an M0 write needs before an LDS
+// direct load.
+__device__ __forceinline__ void dma16_asm(uint8_t* dst, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)dst);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "memory");
+}
+
 // Blocks reach the 8 XCDs round-robin (block b runs on XCD b % 8).  Give each
 // XCD a contiguous range of work ids, and walk the tiles of a K range in
 // groups of `group` tile rows, column by column, so that the tiles running at
@@ -137,7 +160,6 @@ __device__ __forceinline__ void map_work(int bid, int tiles_m, int tiles_n, int 
     tn = local / gm;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 template <int V> using ic = std::integral_constant<int, V>;
@@ -175,8 +197,9 @@ __device__ __forceinline__ void gelu_tanh_staged(f32x4 (&v)[N]) {
         for (int r = 0; r < 4; ++r) v[j][r] = v[j][r] * z[j][r];
 }
 
-template <int WB, int EPI, bool LN, typename TC>
+template <int WB, int EPI, bool LN, typename TC, int KM>
 __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
+    constexpr bool KA = (KM & 1) != 0, KB = (KM & 2) != 0;  // operand stored K-major
     constexpr int BM = Tile<WB>::M, BN = Tile<WB>::M;
     constexpr int NB = Tile<WB>::NB;
     constexpr int UB = Tile<WB>::UNIT_BYTES;
@@ -194,13 +217,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     const int kc = p.K / p.splits;      // this block's K range: [kz kc, (kz+1) kc)
     const int64_t k0 = (int64_t)kz * kc;
 
-    // Buffer resources over this tile's rows of each operand, from its K range on.
-    const uint32_t a_bytes = (uint32_t)(BM * p.lda * 2 - k0 * 2);
-    const uint32_t b_bytes = (uint32_t)(BN * p.ldb * 2 - k0 * 2);
+    // Buffer resources over this tile's rows of each operand, from its K range
+    // on; a K-major operand's resource starts at row k0, column m0 (n0) and
+    // runs to the end of the operand.
+    const uint32_t a_bytes = KA ? (uint32_t)((p.K - k0) * p.lda * 2 - m0 * 2) : (uint32_t)(BM * p.lda * 2 - k0 * 2);
+    const uint32_t b_bytes = KB ? (uint32_t)((p.K - k0) * p.ldb * 2 - n0 * 2) : (uint32_t)(BN * p.ldb * 2 - k0 * 2);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(p.A + m0 * p.lda + k0), (short)0, (int)a_bytes, 0x00020000);
+        const_cast<bf16*>(KA ? p.A + k0 * p.lda + m0 : p.A + m0 * p.lda + k0), (short)0, (int)a_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(p.B + n0 * p.ldb + k0), (short)0, (int)b_bytes, 0x00020000);
+        const_cast<bf16*>(KB ? p.B + k0 * p.ldb + n0 : p.B + n0 * p.ldb + k0), (short)0, (int)b_bytes, 0x00020000);
 
     // Wave w fills rows [w BM/4, (w+1) BM/4) of a unit with LPU loads of 8
     // rows (1 KiB); in load q, lane L fills row w BM/4 + 8 q + L/8 at physical
@@ -218,15 +243,37 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // slot s of the ring
     auto slot = [&](int s) { return ring + s * UB; };
 
+    // K-major operand units: 64 rows (k) of RB = 2 BM bytes (the tile's columns),
+    // 16-byte chunk c of row r at physical chunk c ^ kswz(r).  Wave w fills
+    // rows 16 w .. 16 w + 15 with LPU loads of 1 KiB; in load q lane L lands at
+    // row 16 w + q RPL + L / CPR, physical chunk L % CPR.
+    constexpr int RB = BM * 2, CPR = RB / 16, RPL = 64 / CPR;
+    uint32_t kv_a[KA ? LPU : 1], kv_b[KB ? LPU : 1];
+#pragma unroll
+    for (int q = 0; q < LPU; ++q) {
+        const uint32_t r = (uint32_t)(16 * w + q * RPL + lane / CPR);
+        const uint32_t c = ((uint32_t)(lane % CPR) ^ kswz(r)) << 4;
+        if constexpr (KA) kv_a[q] = r * (uint32_t)(p.lda * 2) + c;
+        if constexpr (KB) kv_b[q] = r * (uint32_t)(p.ldb * 2) + c;
+    }
+
     // load q of the unit of operand `op` (0 = Aop, 1 = Bop) at k0 into slot st
+    // (with a K-major operand every load goes through dma16_asm, since the
+    // transposing reads would wait for any direct load the compiler sees)
     auto load_one = [&](uint8_t* st, int op, int k0, int q) {
         const uint32_t kb = (uint32_t)k0 * 2u;
-        if (op)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + dst_w + q * 1024), 16,
-                                                     (q & 1) ? b_v1 : b_v0, kb + q * b_qstep, 0, 0);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + dst_w + q * 1024), 16,
-                                                     (q & 1) ? a_v1 : a_v0, kb + q * a_qstep, 0, 0);
+        uint8_t* dst = st + dst_w + q * 1024;
+        const __amdgpu_buffer_rsrc_t r = op ? rb : ra;
+        uint32_t voff, soff;
+        if (op) {
+            if constexpr (KB) { voff = kv_b[q]; soff = (uint32_t)k0 * (uint32_t)(p.ldb * 2); }
+            else { voff = (q & 1) ? b_v1 : b_v0; soff = kb + q * b_qstep; }
+        } else {
+            if constexpr (KA) { voff = kv_a[q]; soff = (uint32_t)k0 * (uint32_t)(p.lda * 2); }
+            else { voff = (q & 1) ? a_v1 : a_v0; soff = kb + q * a_qstep; }
+        }
+        if constexpr (KM != 0) dma16_asm(dst, r, voff, soff);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
     };
     auto load_unit = [&](uint8_t* st, int op, int k0) {
 #pragma unroll
@@ -242,6 +289,39 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     const uint32_t rd_b = (uint32_t)((wn * 16 * NB + (lane & 15)) * 128);
     const uint32_t ch0 = (((uint32_t)(lane >> 4)) ^ kr) << 4;
     const uint32_t ch1 = (((uint32_t)(4 + (lane >> 4))) ^ kr) << 4;
+
+    // K-major fragment reads: two ds_read_b64_tr_b16 per 16 x 32 fragment.
+    // In a 16-lane group, lane i addresses row (k) 8 g + 4 h + i / 4 (g the
+    // group, h the half) at column 16 f + 4 (i % 4) of the fragment's 16
+    // columns; the transposing read leaves lane i with column i and the four
+    // rows 8 g + 4 h .. +3, so the two halves are k-slots 8 g .. 8 g + 7, the
+    // same order as a row-major fragment.  kf_*[f] is fragment f's byte offset
+    // in the unit at sub-step 0, h = 0; sub-step kk and half h add
+    // (32 kk + 4 h) RB.
+    uint32_t kf_a[KA ? NB : 1], kf_b[KB ? NB : 1];
+    {
+        const uint32_t li = (uint32_t)lane & 15, g = (uint32_t)lane >> 4;
+        const uint32_t row = 8 * g + (li >> 2);
+        const uint32_t sw = kswz(row);
+#pragma unroll
+        for (int f = 0; f < NB; ++f) {
+            const uint32_t col_a = (uint32_t)(wm * 16 * NB + 16 * f) + 4 * (li & 3);
+            const uint32_t col_b = (uint32_t)(wn * 16 * NB + 16 * f) + 4 * (li & 3);
+            if constexpr (KA) kf_a[f] = row * RB + ((((col_a >> 3) ^ sw)) << 4) + ((col_a & 7) << 1);
+            if constexpr (KB) kf_b[f] = row * RB + ((((col_b >> 3) ^ sw)) << 4) + ((col_b & 7) << 1);
+        }
+    }
+    auto read_frag = [&](const uint8_t* unit, uint32_t off, int kk) -> bf16x8 {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        const uint8_t* q = unit + off + kk * 32 * RB;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q + 4 * RB));
+        bf16x8 r;
+        __builtin_memcpy(&r, &lo, 8);
+        __builtin_memcpy(reinterpret_cast<uint8_t*>(&r) + 8, &hi, 8);
+        return r;
+    };
 
     // acc[i][j]: Aop block i (rows), Bop block j (columns).  With the Bop
     // fragment first, lane l holds row (l & 15) of block i and columns
@@ -279,11 +359,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // offset ch from units ua (Aop) and ub (Bop) into (fn, gn); when
     // `load_op` >= 0, issue the unit of operand load_op at k_load into slot
     // `dst`.
+    auto frag_a = [&](const uint8_t* ua, uint32_t ch, int kk, int f) -> bf16x8 {
+        if constexpr (KA) return read_frag(ua, kf_a[f], kk);
+        else return *reinterpret_cast<const bf16x8*>(ua + rd_a + ch + f * 2048);
+    };
+    auto frag_b = [&](const uint8_t* ub, uint32_t ch, int kk, int f) -> bf16x8 {
+        if constexpr (KB) return read_frag(ub, kf_b[f], kk);
+        else return *reinterpret_cast<const bf16x8*>(ub + rd_b + ch + f * 2048);
+    };
     auto sub_step = [&](const bf16x8 (&fc)[NB], const bf16x8 (&gc)[NB], const uint8_t* ua, const uint8_t* ub,
-                        uint32_t ch, bf16x8 (&fn)[NB], bf16x8 (&gn)[NB], bool do_read, uint8_t* dst, int load_op,
-                        int k_load) {
-        const uint8_t* pa = ua + rd_a + ch;
-        const uint8_t* pb = ub + rd_b + ch;
+                        uint32_t ch, int kk, bf16x8 (&fn)[NB], bf16x8 (&gn)[NB], bool do_read, uint8_t* dst,
+                        int load_op, int k_load) {
 #pragma unroll
         for (int idx = 0; idx < NM; ++idx) {
             const int i = idx / NB, j = idx % NB;
@@ -291,9 +377,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
             if (do_read && idx % RS == 0 && idx / RS < NR) {
                 // fragment reads in consumption order: Aop 0, Bop 0..NB-1, Aop 1..NB-1
                 const int r = idx / RS;
-                if (r == 0) fn[0] = *reinterpret_cast<const bf16x8*>(pa);
-                else if (r <= NB) gn[r - 1] = *reinterpret_cast<const bf16x8*>(pb + (r - 1) * 2048);
-                else fn[r - NB] = *reinterpret_cast<const bf16x8*>(pa + (r - NB) * 2048);
+                if (r == 0) fn[0] = frag_a(ua, ch, kk, 0);
+                else if (r <= NB) gn[r - 1] = frag_b(ub, ch, kk, r - 1);
+                else fn[r - NB] = frag_a(ua, ch, kk, r - NB);
             }
             if (load_op >= 0 && idx % LS == 0) load_one(dst, load_op, k_load, idx / LS);
         }
@@ -321,41 +407,39 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LPU));
     __builtin_amdgcn_s_barrier();
     {
-        const uint8_t* pa = slot(0) + rd_a + ch0;
-        const uint8_t* pb = slot(1) + rd_b + ch0;
-        fa0[0] = *reinterpret_cast<const bf16x8*>(pa);
+        fa0[0] = frag_a(slot(0), ch0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) fb0[j] = *reinterpret_cast<const bf16x8*>(pb + j * 2048);
+        for (int j = 0; j < NB; ++j) fb0[j] = frag_b(slot(1), ch0, 0, j);
 #pragma unroll
-        for (int i = 1; i < NB; ++i) fa0[i] = *reinterpret_cast<const bf16x8*>(pa + i * 2048);
+        for (int i = 1; i < NB; ++i) fa0[i] = frag_a(slot(0), ch0, 0, i);
     }
 
     // step 0: A_2 is already in flight
-    sub_step(fa0, fb0, slot(0), slot(1), ch1, fa1, fb1, true, nullptr, -1, 0);
+    sub_step(fa0, fb0, slot(0), slot(1), ch1, 1, fa1, fb1, true, nullptr, -1, 0);
     barrier_wait(ic<LPU>{});
-    sub_step(fa1, fb1, slot(2), slot(3), ch0, fa0, fb0, true, slot(0), 1, 2 * BK);
+    sub_step(fa1, fb1, slot(2), slot(3), ch0, 0, fa0, fb0, true, slot(0), 1, 2 * BK);
 
     // steps 1 .. nk-3
     int sa = 2;  // slot of A_t
     for (int kt = 1; kt + 2 < nk; ++kt) {
         const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3), sa2 = next(sa, 4);
-        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, fa1, fb1, true, slot(sa2), 0, (kt + 2) * BK);
+        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, 1, fa1, fb1, true, slot(sa2), 0, (kt + 2) * BK);
         barrier_wait(ic<LPU>{});
-        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, fa0, fb0, true, slot(sa), 1, (kt + 2) * BK);
+        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, 0, fa0, fb0, true, slot(sa), 1, (kt + 2) * BK);
         sa = sa1;
     }
     // step nk-2: nothing left to load
     {
         const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3);
-        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, fa1, fb1, true, nullptr, -1, 0);
+        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, 1, fa1, fb1, true, nullptr, -1, 0);
         barrier_wait(ic<0>{});
-        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, fa0, fb0, true, nullptr, -1, 0);
+        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, 0, fa0, fb0, true, nullptr, -1, 0);
         sa = sa1;
     }
     // step nk-1
-    sub_step(fa0, fb0, slot(sa), slot(next(sa, 1)), ch1, fa1, fb1, true, nullptr, -1, 0);
+    sub_step(fa0, fb0, slot(sa), slot(next(sa, 1)), ch1, 1, fa1, fb1, true, nullptr, -1, 0);
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
-    sub_step(fa1, fb1, slot(sa), slot(sa), ch0, fa0, fb0, false, nullptr, -1, 0);
+    sub_step(fa1, fb1, slot(sa), slot(sa), ch0, 0, fa0, fb0, false, nullptr, -1, 0);
     // results of the last MFMAs are read by the epilogue
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
@@ -452,7 +536,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     }
 }
 
-template <int WB, int EPI, typename TC>
+template <int WB, int EPI, typename TC, int KM = 0>
 hipError_t launch_typed(const GemmArgs& g, int splits, hipStream_t stream) {
     constexpr int BM = Tile<WB>::M, BN = Tile<WB>::M;
     FastParams p;
@@ -471,8 +555,12 @@ hipError_t launch_typed(const GemmArgs& g, int splits, hipStream_t stream) {
     p.splits = splits;
     p.c_split_stride = splits > 1 ? g.M * g.N : 0;
     const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n * splits);
-    if (g.ln_mean) gemm_bf16_mfma<WB, EPI, true, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-    else gemm_bf16_mfma<WB, EPI, false, TC><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+    if constexpr (KM != 0)
+        gemm_bf16_mfma<WB, EPI, false, TC, KM><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+    else if (g.ln_mean)
+        gemm_bf16_mfma<WB, EPI, true, TC, 0><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+    else
+        gemm_bf16_mfma<WB, EPI, false, TC, 0><<<dim3(blocks), dim3(256), 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -496,13 +584,19 @@ static int device_cus() {
 // operands, M and N whole tiles, K a whole number (at least three) of
 // 64-wide steps, 16-byte aligned rows, one operand tile's byte offsets below 2^31
 // (buffer offsets), and, with the LayerNorm epilogue, the column sums of Bop.
+// K-major operands: Bop alone (store or GeLU-derivative epilogue) or both
+// (store epilogue), without LayerNorm or the pre-activation stash.
 static bool fits_tile(const GemmArgs& g, int wb) {
     const int64_t tm = 64 * wb;
     if (g.ab_dtype != kBF16) return false;
     if (g.M <= 0 || g.N <= 0 || g.K <= 0) return false;
     if (g.M % tm || g.N % tm || g.K % BK || g.K < 3 * BK) return false;
     if (g.lda % 8 || g.ldb % 8 || !aligned16(g.A) || !aligned16(g.B)) return false;
-    if (tm * g.lda * 2 >= ((int64_t)1 << 31) || tm * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
+    // buffer offsets: a tile's rows of a row-major operand, or all K rows of a K-major one
+    if ((g.a_kmajor ? g.K : tm) * g.lda * 2 >= ((int64_t)1 << 31)) return false;
+    if ((g.b_kmajor ? g.K : tm) * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
+    if (g.a_kmajor && (!g.b_kmajor || g.epi != kEpiStore)) return false;
+    if (g.b_kmajor && ((g.epi != kEpiStore && g.epi != kEpiGeluGrad) || g.ln_mean || g.preact_out)) return false;
     if ((g.M / tm) * (g.N / tm) >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) ||
         g.N >= ((int64_t)1 << 31) || g.K >= ((int64_t)1 << 31))
         return false;
@@ -589,12 +683,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 
 }  // namespace
 
-template <int WB>
-static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
-    if (g.epi == kEpiGelu)
-        return g.preact_out ? launch_typed<WB, kEpiGeluSave, bf16>(g, 1, stream)
-                            : launch_typed<WB, kEpiGelu, bf16>(g, 1, stream);
-    if (g.epi == kEpiGeluGrad) return launch_typed<WB, kEpiGeluGrad, bf16>(g, 1, stream);
+// Store epilogue, with the split-K plan when it applies.
+template <int WB, int KM>
+static hipError_t launch_store(const GemmArgs& g, hipStream_t stream) {
     const int s = split_count(g, WB);
     if (s > 1) {
         // K ranges write fp32 partials, then one pass sums them
@@ -603,7 +694,7 @@ static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
         gp.ldc = g.N;
         gp.c_dtype = kF32;
         gp.R = nullptr;
-        hipError_t e = launch_typed<WB, kEpiStore, float>(gp, s, stream);
+        hipError_t e = launch_typed<WB, kEpiStore, float, KM>(gp, s, stream);
         if (e != hipSuccess) return e;
         const int64_t quads = g.M * g.N / 4;
         const unsigned blocks = (unsigned)std::min<int64_t>((quads + 255) / 256, 8 * (int64_t)device_cus());
@@ -617,8 +708,24 @@ static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
                                                                            static_cast<bf16*>(g.C), g.ldc);
         return hipGetLastError();
     }
-    return g.c_dtype == kF32 ? launch_typed<WB, kEpiStore, float>(g, 1, stream)
-                             : launch_typed<WB, kEpiStore, bf16>(g, 1, stream);
+    return g.c_dtype == kF32 ? launch_typed<WB, kEpiStore, float, KM>(g, 1, stream)
+                             : launch_typed<WB, kEpiStore, bf16, KM>(g, 1, stream);
+}
+
+template <int WB>
+static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
+    // K-major operands (fits_tile admits Bop alone or both, with the store or
+    // GeLU-derivative epilogue and no LayerNorm)
+    if (g.a_kmajor && g.b_kmajor) return launch_store<WB, 3>(g, stream);
+    if (g.b_kmajor) {
+        if (g.epi == kEpiGeluGrad) return launch_typed<WB, kEpiGeluGrad, bf16, 2>(g, 1, stream);
+        return launch_store<WB, 2>(g, stream);
+    }
+    if (g.epi == kEpiGelu)
+        return g.preact_out ? launch_typed<WB, kEpiGeluSave, bf16>(g, 1, stream)
+                            : launch_typed<WB, kEpiGelu, bf16>(g, 1, stream);
+    if (g.epi == kEpiGeluGrad) return launch_typed<WB, kEpiGeluGrad, bf16>(g, 1, stream);
+    return launch_store<WB, 0>(g, stream);
 }
 
 hipError_t launch_gemm_bf16_fast(const GemmArgs& g, hipStream_t stream) {

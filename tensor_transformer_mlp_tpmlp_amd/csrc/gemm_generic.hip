@@ -1,7 +1,7 @@
 // Bounds-checked MFMA GEMM for any shape and for fp32 operands.
 //
-// C[m][n] = epi( sum_k a(m,k) * Bop[n][k] ) with both operands K-contiguous
-// (see GemmArgs).  64x64 output tile per 256-thread workgroup, four waves in
+// C[m][n] = epi( sum_k a(m,k) * Bop[n][k] ) with each operand K-contiguous or
+// stored K-major (see GemmArgs).  64x64 output tile per 256-thread workgroup, four waves in
 // a 2x2 grid, one 32x32 MFMA accumulator per wave, K staged through LDS in
 // steps of 32 with zero fill outside the matrices.  fp32 operands use
 // v_mfma_f32_32x32x2_f32, bf16 operands v_mfma_f32_32x32x16_bf16.
@@ -36,6 +36,7 @@ struct GenericParams {
     int64_t ldaux;
     void* preact;        // kEpiGelu: optional copy of the pre-activation (C's layout and dtype)
     int64_t tiles_n;
+    int a_km, b_km;      // operand stored K-major (see GemmArgs)
 };
 
 // Row pitch of the LDS tiles in elements: fp32 pads by one word against bank
@@ -66,16 +67,19 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GenericParams p) {
 #pragma unroll
         for (int e = 0; e < (GT * GK) / 256; ++e) {
             const int idx = t + 256 * e;
-            const int r = idx / GK, c = idx % GK;
-            const int64_t m = m0 + r, n = n0 + r, k = k0 + c;
+            // consecutive threads walk the operand's contiguous axis
+            const int ra = p.a_km ? idx % GT : idx / GK, ca = p.a_km ? idx / GT : idx % GK;
+            const int rb = p.b_km ? idx % GT : idx / GK, cb = p.b_km ? idx / GT : idx % GK;
+            const int64_t m = m0 + ra, ka = k0 + ca;
+            const int64_t n = n0 + rb, kb = k0 + cb;
             float av = 0.f, bv = 0.f;
-            if (m < p.M && k < p.K) {
-                av = to_f32(A[m * p.lda + k]);
+            if (m < p.M && ka < p.K) {
+                av = to_f32(p.a_km ? A[ka * p.lda + m] : A[m * p.lda + ka]);
                 if constexpr (LN) av = (av - p.mean[m]) * p.rstd[m];
             }
-            if (n < p.N && k < p.K) bv = to_f32(B[n * p.ldb + k]);
-            As[r * P + c] = from_f32<T>(av);
-            Bs[r * P + c] = from_f32<T>(bv);
+            if (n < p.N && kb < p.K) bv = to_f32(p.b_km ? B[kb * p.ldb + n] : B[n * p.ldb + kb]);
+            As[ra * P + ca] = from_f32<T>(av);
+            Bs[rb * P + cb] = from_f32<T>(bv);
         }
         __syncthreads();
         const int ra = (wm * 32 + (lane & 31)) * P;
@@ -131,6 +135,8 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
     p.aux = g.aux; p.ldaux = g.ldaux;
     p.preact = g.preact_out;
     p.tiles_n = (g.N + GT - 1) / GT;
+    p.a_km = g.a_kmajor ? 1 : 0;
+    p.b_km = g.b_kmajor ? 1 : 0;
     const int64_t tiles = ((g.M + GT - 1) / GT) * p.tiles_n;
     if (g.ln_mean)
         gemm_generic_kernel<T, TC, EPI, true><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(p);

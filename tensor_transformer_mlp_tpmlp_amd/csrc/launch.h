@@ -16,7 +16,8 @@ constexpr int kEpiGeluGrad = 2;  // C = acc * GeLU_tanh'(aux), aux M x N in ab_d
 // C[m][n] = epi( sum_k a(m,k) * Bop[n][k] ), m < M, n < N, k < K, where
 // a(m,k) = Aop[m][k], or (Aop[m][k] - ln_mean[m]) * ln_rstd[m] when ln_mean
 // is given.  Aop is M x K row-major (lda), Bop is N x K row-major (ldb): both
-// operands are K-contiguous.  Aop, Bop and R have dtype ab_dtype; C has
+// operands are K-contiguous, unless a_kmajor / b_kmajor say an operand is
+// stored K-major (its transpose row-major).  Aop, Bop and R have dtype ab_dtype; C has
 // c_dtype.  Products accumulate in fp32.
 struct GemmArgs {
     const void* A = nullptr;
@@ -42,6 +43,10 @@ struct GemmArgs {
     // K, a plain store epilogue) is split; the others ignore it.
     void* split_ws = nullptr;
     size_t split_ws_bytes = 0;
+    // K-major operands: with a_kmajor, Aop[m][k] = A[k * lda + m] (A stored
+    // K x M, M contiguous); with b_kmajor, Bop[n][k] = B[k * ldb + n].
+    bool a_kmajor = false;
+    bool b_kmajor = false;
 };
 
 // Bytes of split-K scratch launch_gemm will use for g (0: not split).

@@ -90,48 +90,77 @@ WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard
     return L;
 }
 
-// GEMM shapes of the backward (stand-in aligned pointers), for sizing the
-// split-K scratch they share.
-GemmArgs bwd_shape(int64_t M, int64_t N, int64_t K, int dtype) {
+// The GEMMs of the backward, C[m][n] = sum_k Aop[m][k] Bop[n][k], with every
+// operand read where it lies (K-major where the contraction runs over its
+// rows), so nothing is transposed:
+//   S  = X A:     Aop = X (M x D),          Bop = A^T, packed (F x D)
+//   dS = dY B^T:  Aop = dY (M x D),         Bop = B, i.e. the packed B^T (D x F) read K-major
+//   dX = dS A^T:  Aop = dS (M x F),         Bop = A, i.e. the packed A^T (F x D) read K-major
+//   dA = X^T dS:  Aop = X^T: X read K-major, Bop = dS^T: dS read K-major   (K = M)
+//   dB = H^T dY:  Aop = H^T: H read K-major, Bop = dY^T: dY read K-major   (K = M)
+enum { kBwdS, kBwdDS, kBwdDX, kBwdDA, kBwdDB };
+struct BwdPtrs {
+    const void *X, *dY, *at, *bt, *S;
+    void *H, *dS, *dX, *dA, *dB;
+};
+
+GemmArgs bwd_args(const tpmlp_shards* s, int64_t M, int which, const BwdPtrs& q) {
+    const int64_t D = s->D, F = s->F;
     GemmArgs g;
-    char* const fake = reinterpret_cast<char*>((uintptr_t)256);
-    g.A = fake; g.lda = K;
-    g.B = fake; g.ldb = K;
-    g.M = M; g.N = N; g.K = K;
-    g.C = fake; g.ldc = N; g.c_dtype = dtype;
+    g.ab_dtype = s->dtype;
+    g.c_dtype = s->dtype;
     g.epi = kEpiStore;
-    g.ab_dtype = dtype;
+    switch (which) {
+        case kBwdS:
+            g.A = q.X; g.lda = D; g.B = q.at; g.ldb = D;
+            g.M = M; g.N = F; g.K = D; g.C = const_cast<void*>(q.S); g.ldc = F;
+            break;
+        case kBwdDS:
+            g.A = q.dY; g.lda = D; g.B = q.bt; g.ldb = F; g.b_kmajor = true;
+            g.M = M; g.N = F; g.K = D; g.C = q.dS; g.ldc = F;
+            g.epi = kEpiGeluGrad; g.aux = q.S; g.ldaux = F;
+            break;
+        case kBwdDX:
+            g.A = q.dS; g.lda = F; g.B = q.at; g.ldb = D; g.b_kmajor = true;
+            g.M = M; g.N = D; g.K = F; g.C = q.dX; g.ldc = D;
+            break;
+        case kBwdDA:
+            g.A = q.X; g.lda = D; g.a_kmajor = true; g.B = q.dS; g.ldb = F; g.b_kmajor = true;
+            g.M = D; g.N = F; g.K = M; g.C = q.dA; g.ldc = F;
+            break;
+        default:  // kBwdDB
+            g.A = q.H; g.lda = F; g.a_kmajor = true; g.B = q.dY; g.ldb = D; g.b_kmajor = true;
+            g.M = F; g.N = D; g.K = M; g.C = q.dB; g.ldc = D;
+            break;
+    }
     return g;
 }
 
 // Backward workspace, each segment 256-byte aligned:
-//   A (D x F) and B (F x D) unpacked from the shard buffer,
-//   S = X A (M x F), later dS^T (F x M);  H^T = GeLU(S)^T (F x M);
-//   dS (M x F);  X^T (D x M);  dY^T (D x M);  split-K scratch.
+//   S = X A (M x F, unless the forward kept it);  H = GeLU(S) (M x F);
+//   dS (M x F);  split-K scratch.
 struct BwdLayout {
-    size_t a, b, s_dst, ht, ds, xt, dyt, split, split_bytes, total;
+    size_t s, h, ds, split, split_bytes, total;
 };
 
 BwdLayout bwd_layout(const tpmlp_shards* s, int64_t M) {
     const size_t es = elem_size(s->dtype);
-    const size_t D = (size_t)s->D, F = (size_t)s->F, m = (size_t)M;
+    const size_t F = (size_t)s->F, m = (size_t)M;
     BwdLayout L;
     size_t off = 0;
-    L.a = off; off += round_up(D * F * es);
-    L.b = off; off += round_up(F * D * es);
-    L.s_dst = off; off += round_up(m * F * es);
-    L.ht = off; off += round_up(m * F * es);
+    L.s = off; off += round_up(m * F * es);
+    L.h = off; off += round_up(m * F * es);
     L.ds = off; off += round_up(m * F * es);
-    L.xt = off; off += round_up(D * m * es);
-    L.dyt = off; off += round_up(D * m * es);
     size_t sb = 0;
     if (M > 0) {
-        const int dt = s->dtype;
-        const size_t cand[4] = {gemm_split_bytes(bwd_shape(M, s->F, s->D, dt)),   // S = X A
-                                gemm_split_bytes(bwd_shape(M, s->D, s->F, dt)),   // dX = dS A^T
-                                gemm_split_bytes(bwd_shape(s->D, s->F, M, dt)),   // dA = X^T dS
-                                gemm_split_bytes(bwd_shape(s->F, s->D, M, dt))};  // dB = H^T dY
-        for (size_t c : cand) sb = c > sb ? c : sb;
+        // the split plan depends on shapes, leading dimensions and layouts, not
+        // on addresses: aligned stand-ins
+        char* const fake = reinterpret_cast<char*>((uintptr_t)256);
+        const BwdPtrs q{fake, fake, fake, fake, fake, fake, fake, fake, fake, fake};
+        for (int which = kBwdS; which <= kBwdDB; ++which) {
+            const size_t c = gemm_split_bytes(bwd_args(s, M, which, q));
+            sb = c > sb ? c : sb;
+        }
     }
     L.split = off;
     L.split_bytes = sb;
@@ -387,56 +416,45 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
     const char* at = static_cast<const char*>(s->packed);                     // A^T: F x D
     const char* bt = at + round_up((size_t)D * (size_t)F * eb);              // B^T: D x F
     char* w = static_cast<char*>(workspace);
-    auto gemm = [&](const void* A, int64_t lda, const void* B, int64_t ldb, int64_t m, int64_t n, int64_t k,
-                    void* C, int64_t ldc, int epi, const void* aux) {
-        GemmArgs g;
-        g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
-        g.M = m; g.N = n; g.K = k;
-        g.C = C; g.ldc = ldc; g.c_dtype = dt;
-        g.epi = epi; g.ab_dtype = dt;
-        g.aux = aux; g.ldaux = n;
-        g.split_ws = w + L.split; g.split_ws_bytes = L.split_bytes;
-        return launch_gemm(g, hs);
-    };
 
     if (M == 0) {
         // an empty batch contributes zero weight gradients: K = 0 GEMMs
         // read no operand and write zeros
-        GemmArgs za = bwd_shape(D, F, 0, dt);
-        za.A = dA; za.B = dA; za.C = dA;
-        GemmArgs zb = bwd_shape(F, D, 0, dt);
-        zb.A = dB; zb.B = dB; zb.C = dB;
+        GemmArgs za;
+        za.ab_dtype = dt; za.c_dtype = dt; za.epi = kEpiStore;
+        za.M = D; za.N = F; za.K = 0;
+        za.A = dA; za.B = dA; za.C = dA; za.ldc = F;
+        GemmArgs zb = za;
+        zb.M = F; zb.N = D;
+        zb.A = dB; zb.B = dB; zb.C = dB; zb.ldc = D;
         hipError_t e = launch_gemm_generic(za, hs);
         if (e == hipSuccess) e = launch_gemm_generic(zb, hs);
         return from_hip(e);
     }
 
-    void* Aw = w + L.a;        // A: D x F
-    void* Bw = w + L.b;        // B: F x D
-    void* S = w + L.s_dst;      // S: M x F, later dS^T: F x M
-    void* Ht = w + L.ht;    // H^T: F x M
-    void* dS = w + L.ds;       // dS: M x F
-    void* Xt = w + L.xt;       // X^T: D x M
-    void* dYt = w + L.dyt;     // dY^T: D x M
+    BwdPtrs q;
+    q.X = X; q.dY = dY; q.at = at; q.bt = bt;
+    q.S = preact ? preact : static_cast<const void*>(w + L.s);
+    q.H = w + L.h; q.dS = w + L.ds;
+    q.dX = dX; q.dA = dA; q.dB = dB;
+    auto gemm = [&](int which) {
+        GemmArgs g = bwd_args(s, M, which, q);
+        g.split_ws = w + L.split;
+        g.split_ws_bytes = L.split_bytes;
+        return launch_gemm(g, hs);
+    };
 
-    // The weights in their own layouts ("The split": A is D x F, B is F x D).
-    hipError_t e = launch_transpose(at, D, Aw, F, F, D, eb, hs);
-    if (e == hipSuccess) e = launch_transpose(bt, F, Bw, D, D, F, eb, hs);
-    // S = X A for all shards at once, unless the forward kept it
-    const void* Sv = preact ? preact : S;
-    if (e == hipSuccess && !preact) e = gemm(X, D, at, D, M, F, D, S, F, kEpiStore, nullptr);
+    hipError_t e = hipSuccess;
+    // S = X A for all shards at once, unless the forward kept it; H = GeLU(S)
+    if (!preact) e = gemm(kBwdS);
+    if (e == hipSuccess) e = launch_gelu(q.S, q.H, M * F, dt, hs);
     // dS = (dY B^T) * GeLU'(S): the gradient at every shard's GeLU input
-    if (e == hipSuccess) e = gemm(dY, D, Bw, D, M, F, D, dS, F, kEpiGeluGrad, Sv);
+    if (e == hipSuccess) e = gemm(kBwdDS);
     // dX = sum_i dS_i A_i^T: the K loop over F sums the shards in registers
-    if (e == hipSuccess) e = gemm(dS, F, Aw, F, M, D, F, dX, D, kEpiStore, nullptr);
-    // dA = X^T dS and dB = H^T dY contract over the batch axis M: operands
-    // with M contiguous; H^T = GeLU(S)^T comes straight from S
-    if (e == hipSuccess) e = launch_transpose_gelu(Sv, F, Ht, M, M, F, dt, hs);
-    if (e == hipSuccess) e = launch_transpose(dS, F, S, M, M, F, eb, hs);     // dS^T into S's space
-    if (e == hipSuccess) e = launch_transpose(X, D, Xt, M, M, D, eb, hs);
-    if (e == hipSuccess) e = launch_transpose(dY, D, dYt, M, M, D, eb, hs);
-    if (e == hipSuccess) e = gemm(Xt, M, S, M, D, F, M, dA, F, kEpiStore, nullptr);
-    if (e == hipSuccess) e = gemm(Ht, M, dYt, M, F, D, M, dB, D, kEpiStore, nullptr);
+    if (e == hipSuccess) e = gemm(kBwdDX);
+    // dA = X^T dS and dB = H^T dY contract over the batch axis M
+    if (e == hipSuccess) e = gemm(kBwdDA);
+    if (e == hipSuccess) e = gemm(kBwdDB);
     return from_hip(e);
 }
 

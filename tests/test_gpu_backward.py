@@ -56,6 +56,7 @@ BWD_SHAPES = [
     (200, 136, 264, 3, "bf16"),     # multiples of 8: vector transposes, ragged tiles
     (512, 256, 1024, 4, "bf16"),    # every GEMM on the 128x128 ring kernel
     (1024, 512, 2048, 2, "bf16"),
+    (256, 4096, 3072, 3, "bf16"),   # weight gradients on 256x256 tiles, both operands K-major
 ]
 
 
