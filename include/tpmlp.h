@@ -306,9 +306,9 @@ tpmlp_status tpmlp_attn_pack(const void* Wq, const void* Wk, const void* Wv, con
 void tpmlp_attn_destroy(tpmlp_attn* a);
 
 /* Bytes of device workspace tpmlp_attention needs for batch x seq tokens:
- * the LayerNorm statistics, Q|K|V (batch seq x 3h), V transposed (h x
- * batch seq), the heads' outputs (batch seq x h) when W^O is packed, and
- * the projection GEMMs' split-K scratch.  0 for invalid arguments. */
+ * the LayerNorm statistics, Q|K|V (batch seq x 3h), the heads' outputs
+ * (batch seq x h) when W^O is packed, and the projection GEMMs' split-K
+ * scratch.  0 for invalid arguments. */
 size_t tpmlp_attn_workspace_bytes(const tpmlp_attn* a, int64_t batch, int64_t seq);
 
 /*
@@ -322,7 +322,8 @@ size_t tpmlp_attn_workspace_bytes(const tpmlp_attn* a, int64_t batch, int64_t se
  *          LayerNorm statistics, before the QKV projection, before the
  *          attention kernel and after the last kernel (NULL entries skipped).
  * batch = 0 or seq = 0 is a no-op.  Errors: TPMLP_ERR_NULL, TPMLP_ERR_SHAPE
- * (negative sizes, batch > 65535, batch seq > 2^21, unknown flags), TPMLP_ERR_ALIGN,
+ * (negative sizes, batch > 65535, batch seq > 2^21, (seq + 64) 3h bf16
+ * values of one sequence's Q|K|V reaching 2 GiB, unknown flags), TPMLP_ERR_ALIGN,
  * TPMLP_ERR_WORKSPACE, TPMLP_ERR_HIP; all but the last before any HIP call.
  */
 tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tpmlp_attn* a, void* out, int flags,

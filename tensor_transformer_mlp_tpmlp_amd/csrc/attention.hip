@@ -5,29 +5,28 @@
 //
 // Layouts.  QKV is the projection output, one row per token (batch*seq rows,
 // sequence b in rows b*seq ..), with Q in columns 0..h-1, K in h..2h-1, V in
-// 2h..3h-1 and head j in columns j*64 .. j*64+63 of each (ld = 3h).  V^T is
-// the V block transposed (h rows, one per head column; batch*seq columns),
-// so the P V product reads 8 consecutive keys per lane.  O is written in the
-// concatenated-heads layout (token row, column j*64 + dd), the all_gather-
-// and-cat of "LLM Lab Notes 06", section 2, marker 3, optionally plus the
-// residual x (marker 4).
+// 2h..3h-1 and head j in columns j*64 .. j*64+63 of each (ld = 3h); all three
+// are read where they lie.  O is written in the concatenated-heads layout
+// (token row, column j*64 + dd), the all_gather-and-cat of "LLM Lab Notes
+// 06", section 2, marker 3, optionally plus the residual x (marker 4).
 //
 // One block of 256 threads (4 waves) owns 64 QB query rows of one (sequence,
 // head); wave w owns QB blocks of 16 rows, from row 16 QB w on.  Keys and
-// values stream through LDS in tiles of 64 keys.  Per tile a wave forms S
-// (16 QB x 64) in 8 QB MFMAs, updates the running row maximum and sum
-// (online softmax in the log2 domain, fp32), rounds P to bf16 and
-// accumulates O (16 QB x 64) in 8 QB MFMAs; each K and V^T fragment read
-// from LDS feeds QB of them.
+// values stream through LDS in tiles of 64 tokens (64 rows of 128 bytes
+// each).  Per tile a wave forms S (16 QB x 64) in 8 QB MFMAs, updates the
+// running row maximum and sum (online softmax in the log2 domain, fp32),
+// rounds P to bf16 and accumulates O (16 QB x 64) in 8 QB MFMAs; each K and
+// V fragment read from LDS feeds QB of them.
 //
 // MFMA operand order: the first operand's rows index the result's rows as
 // seen by the lanes, so S = mfma(K frag, Q frag) leaves lane l with query
 // row l & 15 and keys 4 (l >> 4) + r of a 16-key block, and
-// O = mfma(V^T frag, P frag) leaves it with query row l & 15 and columns
+// O = mfma(V frag, P frag) leaves it with query row l & 15 and head columns
 // 4 (l >> 4) + r.  A lane's 8 k-slots of P are therefore keys {4g .. 4g+3}
 // of the even 16-key block and {16 + 4g .. 16 + 4g + 3} of the odd one
-// (g = l >> 4); the V^T fragment is read with the same key order, which is
-// all the contraction needs.
+// (g = l >> 4).  The V fragment (head column l & 15, those 8 keys) comes from
+// the V rows in LDS by two transposing reads (ds_read_b64_tr_b16), whose
+// per-lane addresses pick exactly those keys.
 #include <type_traits>
 
 #include "device_common.h"
@@ -43,15 +42,18 @@ constexpr int kDH = 64;      // head width
 constexpr int kKT = 64;      // keys per tile
 constexpr int kRowB = 128;   // bytes per LDS row (64 bf16)
 
-// 16-byte chunk swizzle of a 128-byte LDS row: the 16 lanes of a read pass
-// hit 16 distinct chunk slots for the 16-row fragment pattern.
+// 16-byte chunk swizzles of the 128-byte LDS rows.  K tile (16-byte fragment
+// reads of 16 rows): the 16 lanes of a read pass hit 16 distinct chunk
+// slots.  V tile (transposing reads of 32 bytes from each of 16 consecutive
+// rows): the 32-byte windows of those rows cover the 256-byte bank space
+// twice.
 __device__ __forceinline__ int swz(int row) { return ((row & 8) >> 2) | ((row & 2) << 1); }
+__device__ __forceinline__ int vswz(int row) { return 2 * ((row >> 1) & 3); }
 
 struct AttnParams {
     const bf16* qkv;   // batch*seq x 3h
     int64_t ldq;       // 3h
-    const bf16* vt;    // h x batch*seq
-    int64_t ldv;       // batch*seq
+    int64_t tokens;    // batch*seq
     const bf16* x;     // residual, batch*seq x h (nullptr: none)
     int64_t ldx;
     bf16* out;         // batch*seq x h
@@ -79,10 +81,22 @@ struct AttnParams {
 // wave either rescales all its rows (each with its own factor) or none.
 constexpr float kLazy = 8.0f;
 
+// vo[db]: this lane's byte offset in the V tile of its transposing read for
+// head-column block db, keys 4 g .. 4 g + 3 (add 16 rows for keys 16 + 4 g ..,
+// 32 rows per 32-key chunk).
+__device__ __forceinline__ void v_offsets(int g, int li, uint32_t (&vo)[4]) {
+    const int row = 4 * g + (li >> 2);
+    const int vs = vswz(row);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+        vo[db] = (uint32_t)(row * kRowB + (((2 * db + ((li & 3) >> 1)) ^ vs) << 4) + ((li & 1) << 3));
+}
+
 template <int QB>
 __device__ __forceinline__ void attn_tile(const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb,
                                           const bf16x8 (&qf)[QB][2], f32x4 (&o)[QB][4], f32x4 (&ls)[QB],
-                                          float (&m_run)[QB], int kv0, int seq, float c_log2, int g, int li) {
+                                          float (&m_run)[QB], int kv0, int seq, float c_log2, int g, int li,
+                                          const uint32_t (&vo)[4]) {
     // S = Q K^T for the 64 keys of the tile: lane holds query li of block i, keys 16 jb + 4 g + r
     f32x4 s[QB][4];
 #pragma unroll
@@ -157,21 +171,18 @@ __device__ __forceinline__ void attn_tile(const uint8_t* __restrict__ kb, const 
 #pragma unroll
         for (int c = 0; c < 2; ++c) ls[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[i][c], ls[i], 0, 0, 0);
 
-    // O += P V: V^T rows are head columns; keys in the P fragment's order
+    // O += P V: the V fragment of head columns 16 db .. +15 holds, in lane l,
+    // column 16 db + (l & 15) at the keys of P's k-slots
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        const int r = 16 * db + li;
-        const uint8_t* vrow = &vb[r * kRowB];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            // keys 32c + 4g .. +3 and 32c + 16 + 4g .. +3: 8-byte halves of 16-byte chunks
-            const int ch0 = 4 * c + (g >> 1), ch1 = 4 * c + 2 + (g >> 1);
-            const int half = (g & 1) << 3;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ((ch0 ^ swz(r)) << 4) + half);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ((ch1 ^ swz(r)) << 4) + half);
-            const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+            const uint8_t* vp = vb + vo[db] + 32 * c * kRowB;
+            const v4s lo = lds_read_tr16(vp);
+            const v4s hi = lds_read_tr16(vp + 16 * kRowB);
             bf16x8 vf;
-            __builtin_memcpy(&vf, &raw, 16);
+            __builtin_memcpy(&vf, &lo, 8);
+            __builtin_memcpy(reinterpret_cast<uint8_t*>(&vf) + 8, &hi, 8);
 #pragma unroll
             for (int i = 0; i < QB; ++i)
                 o[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i][c], o[i][db], 0, 0, 0);
@@ -226,104 +237,24 @@ __device__ __forceinline__ void store_o(const AttnParams& p, int64_t tok0, int q
     }
 }
 
-template <int QB>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kKT * kRowB];
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][kDH * kRowB];
-
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int w = t >> 6;
-    const int g = lane >> 4;
-    const int li = lane & 15;
-    const int seq = p.seq;
-    const int qw = blockIdx.x * 64 * QB + 16 * QB * w;  // this wave's first query row
-    const int head = blockIdx.y;
-    const int64_t tok0 = (int64_t)blockIdx.z * seq;  // first token row of this sequence
-    const bool vt_vec = (seq & 7) == 0;              // 16-byte V^T chunks stay in one sequence
-
-    bf16x8 qf[QB][2];
-    load_q<QB>(p, tok0, qw, g, li, qf, head);
-
-    // tile loader: thread t moves K chunks (row t/8, t/8+32; chunk t%8) and
-    // V^T chunks (head column t/8, t/8+32; keys 8 (t%8) ..), 16 bytes each
-    const int lrow = t >> 3, lch = t & 7;
-    u32x4 kreg[2], vreg[2];
-    auto load_tile = [&](int kv0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = lrow + 32 * i;
-            u32x4 kv = {0u, 0u, 0u, 0u};
-            if (kv0 + r < seq)
-                kv = *reinterpret_cast<const u32x4*>(p.qkv + (tok0 + kv0 + r) * p.ldq + p.h + head * kDH + 8 * lch);
-            kreg[i] = kv;
-            const bf16* vsrc = p.vt + (int64_t)(head * kDH + r) * p.ldv + tok0 + kv0 + 8 * lch;
-            const int valid = seq - (kv0 + 8 * lch);
-            u32x4 vv = {0u, 0u, 0u, 0u};
-            if (valid >= 8 && vt_vec) {
-                vv = *reinterpret_cast<const u32x4*>(vsrc);
-            } else if (valid > 0) {
-                bf16 e[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) e[k] = k < valid ? vsrc[k] : static_cast<bf16>(0.0f);
-                __builtin_memcpy(&vv, e, 16);
-            }
-            vreg[i] = vv;
-        }
-    };
-    auto store_tile = [&](int b) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = lrow + 32 * i;
-            *reinterpret_cast<u32x4*>(&kbuf[b][r * kRowB + ((lch ^ swz(r)) << 4)]) = kreg[i];
-            *reinterpret_cast<u32x4*>(&vbuf[b][r * kRowB + ((lch ^ swz(r)) << 4)]) = vreg[i];
-        }
-    };
-
-    f32x4 o[QB][4], ls[QB];
-    float m_run[QB];
-#pragma unroll
-    for (int i = 0; i < QB; ++i) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        ls[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run[i] = -__builtin_inff();
-    }
-
-    const int ntiles = (seq + kKT - 1) / kKT;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        const int b = it & 1;
-        const int kv0 = it * kKT;
-        if (it + 1 < ntiles) load_tile(kv0 + kKT);
-        attn_tile<QB>(kbuf[b], vbuf[b], qf, o, ls, m_run, kv0, seq, p.scale_log2, g, li);
-        if (it + 1 < ntiles) store_tile(b ^ 1);
-        __syncthreads();
-    }
-    store_o<QB>(p, tok0, qw, g, li, head, o, ls);
-}
-
 // s_waitcnt immediates (gfx9): vmcnt in bits [3:0] and [15:14], expcnt and
 // lgkmcnt left at their maxima (no wait) unless asked for.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
 
-typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kStages = 3;
-constexpr int kTileB = kKT * kRowB;  // 8 KiB: one K tile or one V^T tile
+constexpr int kTileB = kKT * kRowB;  // 8 KiB: one K tile or one V tile
 
-// The same computation with the key and value tiles moved by direct
-// global-to-LDS loads (16 bytes per lane) through a ring of three stages, so
-// each tile's loads are issued two tiles ahead of its use and no registers
-// stage them.  Wave w fills LDS rows 16 w .. 16 w + 15 of each tile in two
-// loads of 8 rows; lane L lands at row 16 w + 8 q + L/8, physical chunk L % 8,
-// so it reads the logical chunk (L % 8) ^ swz(row) of that row.  Buffer
-// resources bound every read to the end of QKV and V^T: rows past the last
-// sequence read as zero, and keys of the next sequence are masked like any
-// key past the sequence end.  Requires seq % 8 == 0 (16-byte aligned V^T
-// chunks) and both buffers below 2 GiB.
+// Key and value tiles move by direct global-to-LDS loads (16 bytes per
+// lane) through a ring of three stages, so each tile's loads are issued two
+// tiles ahead of its use and no registers stage them.  Wave w fills LDS rows
+// 16 w .. 16 w + 15 of each tile in two loads of 8 rows; lane L lands at row
+// 16 w + 8 q + L/8, physical chunk L % 8, so it reads the logical chunk
+// (L % 8) ^ swizzle(row) of that row.  Buffer resources cover this
+// sequence's rows (plus one tile) up to the end of QKV: rows past the last
+// token read as zero, and rows of the next sequence are masked (keys) or
+// multiplied by P = 0 (values) like any row past the sequence end.  Requires
+// (seq + 64) rows of QKV below 2 GiB (buffer offsets).
 template <int QB>
 __global__ __launch_bounds__(256) void attn_fwd_ring_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][2][kTileB];
@@ -337,32 +268,35 @@ __global__ __launch_bounds__(256) void attn_fwd_ring_kernel(AttnParams p) {
     const int qw = blockIdx.x * 64 * QB + 16 * QB * w;
     const int head = blockIdx.y;
     const int64_t tok0 = (int64_t)blockIdx.z * seq;
-    const int64_t M = p.ldv;
 
     bf16x8 qf[QB][2];
     load_q<QB>(p, tok0, qw, g, li, qf, head);
+    uint32_t vo[4];
+    v_offsets(g, li, vo);
 
     const int64_t k_off = tok0 * p.ldq + p.h + (int64_t)head * kDH;
-    const int64_t v_off = (int64_t)head * kDH * p.ldv + tok0;
+    const int64_t v_off = k_off + p.h;
+    const int64_t total = p.tokens * p.ldq;
+    const int64_t span = (int64_t)(seq + kKT) * p.ldq;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(p.qkv + k_off), (short)0, (int)((M * p.ldq - k_off) * 2), 0x00020000);
+        const_cast<bf16*>(p.qkv + k_off), (short)0, (int)(min(total - k_off, span) * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(p.vt + v_off), (short)0, (int)((p.h * p.ldv - v_off) * 2), 0x00020000);
+        const_cast<bf16*>(p.qkv + v_off), (short)0, (int)(min(total - v_off, span) * 2), 0x00020000);
     const int r0 = 16 * w + (lane >> 3);
     const int r1 = r0 + 8;
     const int pc = lane & 7;
     const uint32_t kv_0 = (uint32_t)(r0 * p.ldq * 2 + ((pc ^ swz(r0)) << 4));
     const uint32_t kv_1 = (uint32_t)(r1 * p.ldq * 2 + ((pc ^ swz(r1)) << 4));
-    const uint32_t vv_0 = (uint32_t)(r0 * p.ldv * 2 + ((pc ^ swz(r0)) << 4));
-    const uint32_t vv_1 = (uint32_t)(r1 * p.ldv * 2 + ((pc ^ swz(r1)) << 4));
+    const uint32_t vv_0 = (uint32_t)(r0 * p.ldq * 2 + ((pc ^ vswz(r0)) << 4));
+    const uint32_t vv_1 = (uint32_t)(r1 * p.ldq * 2 + ((pc ^ vswz(r1)) << 4));
     const int dst0 = 16 * w * kRowB, dst1 = dst0 + 8 * kRowB;
 
     auto issue = [&](int kv0, int st) {
-        const uint32_t ks = (uint32_t)(kv0 * p.ldq * 2), vs = (uint32_t)(kv0 * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(&ring[st][0][dst0]), 16, kv_0, ks, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(&ring[st][0][dst1]), 16, kv_1, ks, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(&ring[st][1][dst0]), 16, vv_0, vs, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(&ring[st][1][dst1]), 16, vv_1, vs, 0, 0);
+        const uint32_t so = (uint32_t)(kv0 * p.ldq * 2);
+        dma16_asm(&ring[st][0][dst0], rk, kv_0, so);
+        dma16_asm(&ring[st][0][dst1], rk, kv_1, so);
+        dma16_asm(&ring[st][1][dst0], rv, vv_0, so);
+        dma16_asm(&ring[st][1][dst1], rv, vv_1, so);
     };
 
     f32x4 o[QB][4], ls[QB];
@@ -390,7 +324,7 @@ __global__ __launch_bounds__(256) void attn_fwd_ring_kernel(AttnParams p) {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __builtin_amdgcn_s_barrier();
         if (it + 2 < ntiles) issue((it + 2) * kKT, st == 0 ? 2 : st - 1);
-        attn_tile<QB>(ring[st][0], ring[st][1], qf, o, ls, m_run, it * kKT, seq, p.scale_log2, g, li);
+        attn_tile<QB>(ring[st][0], ring[st][1], qf, o, ls, m_run, it * kKT, seq, p.scale_log2, g, li, vo);
         st = st == 2 ? 0 : st + 1;
     }
     store_o<QB>(p, tok0, qw, g, li, head, o, ls);
@@ -398,14 +332,16 @@ __global__ __launch_bounds__(256) void attn_fwd_ring_kernel(AttnParams p) {
 
 }  // namespace
 
-hipError_t launch_attention(const void* qkv, int64_t ldq, const void* vt, int64_t ldv, const void* x, int64_t ldx,
-                            void* out, int64_t ldo, int64_t batch, int64_t seq, int64_t heads,
-                            hipStream_t stream) {
+bool attention_fits(int64_t seq, int64_t heads) {
+    return (seq + kKT) * 3 * heads * kDH * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_attention(const void* qkv, int64_t ldq, const void* x, int64_t ldx, void* out, int64_t ldo,
+                            int64_t batch, int64_t seq, int64_t heads, hipStream_t stream) {
     AttnParams p;
     p.qkv = static_cast<const bf16*>(qkv);
     p.ldq = ldq;
-    p.vt = static_cast<const bf16*>(vt);
-    p.ldv = ldv;
+    p.tokens = batch * seq;
     p.x = static_cast<const bf16*>(x);
     p.ldx = ldx;
     p.out = static_cast<bf16*>(out);
@@ -413,17 +349,13 @@ hipError_t launch_attention(const void* qkv, int64_t ldq, const void* vt, int64_
     p.h = heads * kDH;
     p.seq = (int)seq;
     p.scale_log2 = (float)(kLog2e / 8.0);  // 1 / sqrt(64) = 1/8
-    const int64_t M = batch * seq;
-    const bool ring = seq % 8 == 0 && M * ldq * 2 < ((int64_t)1 << 31) && p.h * ldv * 2 < ((int64_t)1 << 31);
+    if (!attention_fits(seq, heads)) return hipErrorInvalidValue;
     // 64 query rows per wave for long sequences (each K/V fragment feeds four
     // MFMAs); 32 otherwise, which keeps more blocks for short ones
     auto launch = [&](auto qb) {
         constexpr int QB = decltype(qb)::value;
         const dim3 grid((unsigned)((seq + 64 * QB - 1) / (64 * QB)), (unsigned)heads, (unsigned)batch);
-        if (ring)
-            attn_fwd_ring_kernel<QB><<<grid, dim3(256), 0, stream>>>(p);
-        else
-            attn_fwd_kernel<QB><<<grid, dim3(256), 0, stream>>>(p);
+        attn_fwd_ring_kernel<QB><<<grid, dim3(256), 0, stream>>>(p);
     };
     if (seq >= 1024)
         launch(std::integral_constant<int, 4>{});

@@ -67,10 +67,10 @@ GemmArgs proj_shape(int64_t M, int64_t N, int64_t K) {
     return g;
 }
 
-// Workspace: [mean: M fp32][rstd: M fp32][QKV: M x 3h][V^T: h x M]
+// Workspace: [mean: M fp32][rstd: M fp32][QKV: M x 3h]
 // [O: M x h, with W^O][split-K scratch], 256-byte aligned segments.
 struct WsLayout {
-    size_t mean, rstd, qkv, vt, o, split, split_bytes, total;
+    size_t mean, rstd, qkv, o, split, split_bytes, total;
 };
 
 WsLayout ws_layout(const tpmlp_attn* a, int64_t M) {
@@ -80,7 +80,6 @@ WsLayout ws_layout(const tpmlp_attn* a, int64_t M) {
     L.mean = off; off += round_up(m * 4);
     L.rstd = off; off += round_up(m * 4);
     L.qkv = off; off += round_up(m * 3 * h * 2);
-    L.vt = off; off += round_up(h * m * 2);
     L.o = off; if (a->has_wo) off += round_up(m * h * 2);
     size_t sb = 0;
     if (M > 0) {
@@ -160,6 +159,7 @@ tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tp
     if (!a) return TPMLP_ERR_NULL;
     if (batch < 0 || seq < 0 || seq > kMaxTokens || (seq > 0 && batch > kMaxTokens / seq)) return TPMLP_ERR_SHAPE;
     if (batch > kMaxBatch) return TPMLP_ERR_SHAPE;
+    if (seq > 0 && !attention_fits(seq, a->heads)) return TPMLP_ERR_SHAPE;
     if (flags & ~(TPMLP_ATTN_LAYERNORM | TPMLP_ATTN_RESIDUAL)) return TPMLP_ERR_SHAPE;
     const float eps = ln_eps > 0.f ? ln_eps : 1e-5f;
     if (!(eps < 1e30f)) return TPMLP_ERR_SHAPE;
@@ -181,7 +181,6 @@ tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tp
     float* mean = reinterpret_cast<float*>(w + L.mean);
     float* rstd = reinterpret_cast<float*>(w + L.rstd);
     char* qkv = w + L.qkv;
-    char* vt = w + L.vt;
 
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     if (events)
@@ -204,16 +203,14 @@ tpmlp_status tpmlp_attention(const void* x, int64_t batch, int64_t seq, const tp
         g.split_ws_bytes = L.split_bytes;
         e = launch_gemm(g, hs);
     }
-    // V^T (h x M): the P V product contracts over keys
-    if (e == hipSuccess) e = launch_transpose(qkv + (size_t)2 * h * 2, 3 * h, vt, M, M, h, 2, hs);
     if (e == hipSuccess) e = mark(2);
     if (e == hipSuccess) {
         if (!a->has_wo) {
             // the heads' outputs side by side (all_gather + cat), plus x
-            e = launch_attention(qkv, 3 * h, vt, M, resid ? x : nullptr, h, out, h, batch, seq, a->heads, hs);
+            e = launch_attention(qkv, 3 * h, resid ? x : nullptr, h, out, h, batch, seq, a->heads, hs);
         } else {
             char* o = w + L.o;
-            e = launch_attention(qkv, 3 * h, vt, M, nullptr, h, o, h, batch, seq, a->heads, hs);
+            e = launch_attention(qkv, 3 * h, nullptr, h, o, h, batch, seq, a->heads, hs);
             // row-parallel output projection: the K loop over h sums every rank's part
             if (e == hipSuccess) {
                 GemmArgs g = proj_shape(M, h, h);

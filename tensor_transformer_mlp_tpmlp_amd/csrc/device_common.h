@@ -49,6 +49,35 @@ __device__ __forceinline__ float gelu_tanh_grad(float x) {
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane direct load from a buffer resource into LDS at the
+// wave-uniform address dst (lane L's 16 bytes land at dst + 16 L), written
+// out so that the compiler does not see an LDS write in flight: it would
+// otherwise wait for every such load before each transposing LDS read
+// (ds_read_b64_tr_b16), since it cannot tell LDS buffers apart.  Callers order
+// these loads against their readers themselves (vmcnt waits and barriers).
+// M0 holds the LDS address; the s_nop is the wait state an M0 write needs
+// before an LDS direct load.
+__device__ __forceinline__ void dma16_asm(uint8_t* dst, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)dst);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "memory");
+}
+
+// Transposing LDS read of four 16-bit values (ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, lane i supplies the address of 4 consecutive
+// elements (row i / 4 of a 4 x 16 block when the addresses are set up as
+// row (i / 4), column 4 (i % 4)); lane j receives, for k = 0..3, element
+// j % 4 of the four elements addressed by lane 4 k + j / 4.  With lane 4 k + q
+// addressing row r_k at column c0 + 4 q, lane j receives column c0 + j of
+// rows r_0 .. r_3.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4s lds_read_tr16(const uint8_t* p) {
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }

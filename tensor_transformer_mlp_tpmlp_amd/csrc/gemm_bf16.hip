@@ -122,20 +122,6 @@ __device__ __forceinline__ uint32_t lds_key(uint32_t r) { return ((r & 8) >> 2) 
 // distinct 32-byte bank groups.
 __device__ __forceinline__ uint32_t kswz(uint32_t r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One 16-byte-per-lane direct load into LDS at the wave-uniform address dst,
-// written out so that the compiler does not see an LDS write in flight: it
-// would otherwise wait for every such load before each transposing LDS read
-// (it cannot tell the ring slots apart).  The kernels order these loads
-// against their readers themselves (vmcnt waits and barriers).  M0 holds the
-// LDS address; the s_nop is the wait state an M0 write needs before an LDS
-// direct load.
-__device__ __forceinline__ void dma16_asm(uint8_t* dst, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)dst);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(r), "s"(soff)
-                 : "memory");
-}
 
 // Blocks reach the 8 XCDs round-robin (block b runs on XCD b % 8).  Give each
 // XCD a contiguous range of work ids, and walk the tiles of a K range in
@@ -312,11 +298,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
         }
     }
     auto read_frag = [&](const uint8_t* unit, uint32_t off, int kk) -> bf16x8 {
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) v4s lds_v4s;
         const uint8_t* q = unit + off + kk * 32 * RB;
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q + 4 * RB));
+        const v4s lo = lds_read_tr16(q);
+        const v4s hi = lds_read_tr16(q + 4 * RB);
         bf16x8 r;
         __builtin_memcpy(&r, &lo, 8);
         __builtin_memcpy(reinterpret_cast<uint8_t*>(&r) + 8, &hi, 8);

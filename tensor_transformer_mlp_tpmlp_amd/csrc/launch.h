@@ -65,9 +65,11 @@ hipError_t launch_ln_stats(const void* x, int64_t M, int64_t D, int dtype, float
                            float* rstd, hipStream_t stream);
 hipError_t launch_ln_apply(const float* x, int64_t M, int64_t D, float eps, void* out, int out_dtype,
                            hipStream_t stream);
-hipError_t launch_attention(const void* qkv, int64_t ldq, const void* vt, int64_t ldv, const void* x, int64_t ldx,
-                            void* out, int64_t ldo, int64_t batch, int64_t seq, int64_t heads,
-                            hipStream_t stream);
+// Whether one sequence's rows of Q|K|V (plus one key tile) stay below the
+// 2 GiB that the attention kernel's buffer offsets address.
+bool attention_fits(int64_t seq, int64_t heads);
+hipError_t launch_attention(const void* qkv, int64_t ldq, const void* x, int64_t ldx, void* out, int64_t ldo,
+                            int64_t batch, int64_t seq, int64_t heads, hipStream_t stream);
 hipError_t launch_rowsum(const void* x, int64_t rows, int64_t cols, int dtype, float* out, hipStream_t stream);
 hipError_t launch_transpose(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
                             int elem_bytes, hipStream_t stream);

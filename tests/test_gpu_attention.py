@@ -3,10 +3,9 @@ oracle ``oracle.attention_oracle.attention_half``, through the C ABI.
 
 The output with the residual is compared together with the attention term
 alone (residual off), so that x cannot mask an attention error.  Shapes
-cover one token, sequences shorter than a key tile, ragged tiles with and
-without 8-token alignment (the two V^T load forms), several tiles, both
-output forms (concatenated heads; row-parallel W^O) and the attention
-workloads at their full sizes.
+cover one token, sequences shorter than a key tile, ragged tiles, several
+tiles, 32 and 64 query rows per wave, both output forms (concatenated heads;
+row-parallel W^O) and the attention workloads at their full sizes.
 """
 
 import ctypes
@@ -53,15 +52,15 @@ def _check(inp, batch, seq, heads, p, with_wo, layernorm, what):
 ATTN_SHAPES = [
     # (batch, seq, heads, p, sw scale)
     (1, 1, 1, 1, 1.0),       # one token: softmax of one key
-    (2, 5, 2, 2, 1.0),       # shorter than a tile, seq % 8 != 0
+    (2, 5, 2, 2, 1.0),       # shorter than a tile
     (2, 64, 4, 2, 1.0),      # exactly one tile
-    (3, 100, 4, 4, 1.0),     # two tiles, ragged, seq % 8 != 0
-    (2, 136, 2, 1, 1.0),     # three tiles, ragged, seq % 8 == 0 (LDS-ring kernel)
-    (3, 200, 2, 2, 1.0),     # four tiles, ragged, seq % 8 == 0 (LDS-ring kernel)
+    (3, 100, 4, 4, 1.0),     # two tiles, ragged, rows not 16-byte aligned in token count
+    (2, 136, 2, 1, 1.0),     # three tiles, ragged
+    (3, 200, 2, 2, 1.0),     # four tiles, ragged
     (2, 300, 4, 2, 1.0),     # five tiles
-    (1, 512, 2, 1, 1.0),     # eight full tiles (LDS-ring kernel)
-    (1, 1024, 2, 2, 1.0),    # 64 query rows per wave (LDS-ring kernel)
-    (2, 1100, 1, 1, 1.0),    # 64 query rows per wave, ragged, seq % 8 != 0
+    (1, 512, 2, 1, 1.0),     # eight full tiles, one sequence (reads run past the last token)
+    (1, 1024, 2, 2, 1.0),    # 64 query rows per wave
+    (2, 1100, 1, 1, 1.0),    # 64 query rows per wave, ragged
 ]
 
 
