@@ -39,10 +39,13 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-# Per-file backend options.  attention.hip: MFMA results in VGPRs (the
-# softmax reads and rescales them every tile; in AGPRs each access would
-# need a copy).
-EXTRA_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file options.  attention.hip: MFMA results in VGPRs (the softmax reads
+# and rescales them every tile; in AGPRs each access would need a copy), and
+# the floating-point mode without IEEE NaN quieting, so that a maximum is one
+# v_max_f32 rather than two operands quieted first (a third of the kernel's
+# maxima were quieting operations); NaN inputs to the attention half give
+# unspecified results.
+EXTRA_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _compile(src: str) -> str:

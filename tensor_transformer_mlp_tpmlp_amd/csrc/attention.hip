@@ -81,6 +81,22 @@ struct AttnParams {
 // wave either rescales all its rows (each with its own factor) or none.
 constexpr float kLazy = 8.0f;
 
+// max(x[l], x[l ^ D]) in every lane l, D = 16 or 32, through the gfx950 lane
+// swaps (each returns the pair {x[l], x[l ^ D]} in its two results; measured
+// with an in-bounds probe): two VALU operations instead of an LDS permute.
+template <int D>
+__device__ __forceinline__ float pair_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if constexpr (D == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    } else {
+        static_assert(D == 16, "lane distance 16 or 32");
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+}
+
 // vo[db]: this lane's byte offset in the V tile of its transposing read for
 // head-column block db, keys 4 g .. 4 g + 3 (add 16 rows for keys 16 + 4 g ..,
 // 32 rows per 32-key chunk).
@@ -134,8 +150,8 @@ __device__ __forceinline__ void attn_tile(const uint8_t* __restrict__ kb, const 
 #pragma unroll
         for (int jb = 1; jb < 4; ++jb)
             mt = fmaxf(fmaxf(mt, fmaxf(s[i][jb][0], s[i][jb][1])), fmaxf(s[i][jb][2], s[i][jb][3]));
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = pair_max<16>(mt);
+        mt = pair_max<32>(mt);
         mc[i] = mt * c_log2;
         raise |= mc[i] > m_run[i] + kLazy;
     }
@@ -278,10 +294,8 @@ __global__ __launch_bounds__(256) void attn_fwd_ring_kernel(AttnParams p) {
     const int64_t v_off = k_off + p.h;
     const int64_t total = p.tokens * p.ldq;
     const int64_t span = (int64_t)(seq + kKT) * p.ldq;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(p.qkv + k_off), (short)0, (int)(min(total - k_off, span) * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(p.qkv + v_off), (short)0, (int)(min(total - v_off, span) * 2), 0x00020000);
+    const u32x4 rk = buffer_rsrc_sgpr(p.qkv + k_off, (uint32_t)(min(total - k_off, span) * 2));
+    const u32x4 rv = buffer_rsrc_sgpr(p.qkv + v_off, (uint32_t)(min(total - v_off, span) * 2));
     const int r0 = 16 * w + (lane >> 3);
     const int r1 = r0 + 8;
     const int pc = lane & 7;

@@ -51,7 +51,21 @@ __device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One 16-byte-per-lane direct load from a buffer resource into LDS at the
+// A raw buffer resource (base address, no stride, num_records bytes, the
+// default data format) as four wave-uniform dwords, for the inline
+// assembly below.  Each dword goes through readfirstlane so that it is an
+// SGPR value whatever the compiler inferred about its uniformity.
+__device__ __forceinline__ u32x4 buffer_rsrc_sgpr(const void* base, uint32_t num_records) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(num_records);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// One 16-byte-per-lane direct load from buffer resource r into LDS at the
 // wave-uniform address dst (lane L's 16 bytes land at dst + 16 L), written
 // out so that the compiler does not see an LDS write in flight: it would
 // otherwise wait for every such load before each transposing LDS read
@@ -59,9 +73,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // these loads against their readers themselves (vmcnt waits and barriers).
 // M0 holds the LDS address; the s_nop is the wait state an M0 write needs
 // before an LDS direct load.
-__device__ __forceinline__ void dma16_asm(uint8_t* dst, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)dst);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(r), "s"(soff)
+__device__ __forceinline__ void dma16_asm(uint8_t* dst, u32x4 r, uint32_t voff, uint32_t soff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void*)dst));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(r),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
                  : "memory");
 }
 

@@ -229,6 +229,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // slot s of the ring
     auto slot = [&](int s) { return ring + s * UB; };
 
+    // the same resources as SGPR dwords for the inline-assembly loads
+    u32x4 ra4 = {}, rb4 = {};
+    if constexpr (KM != 0) {
+        ra4 = buffer_rsrc_sgpr(KA ? p.A + k0 * p.lda + m0 : p.A + m0 * p.lda + k0, a_bytes);
+        rb4 = buffer_rsrc_sgpr(KB ? p.B + k0 * p.ldb + n0 : p.B + n0 * p.ldb + k0, b_bytes);
+    }
+
     // K-major operand units: 64 rows (k) of RB = 2 BM bytes (the tile's columns),
     // 16-byte chunk c of row r at physical chunk c ^ kswz(r).  Wave w fills
     // rows 16 w .. 16 w + 15 with LPU loads of 1 KiB; in load q lane L lands at
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
             if constexpr (KA) { voff = kv_a[q]; soff = (uint32_t)k0 * (uint32_t)(p.lda * 2); }
             else { voff = (q & 1) ? a_v1 : a_v0; soff = kb + q * a_qstep; }
         }
-        if constexpr (KM != 0) dma16_asm(dst, r, voff, soff);
+        if constexpr (KM != 0) dma16_asm(dst, op ? rb4 : ra4, voff, soff);
         else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
     };
     auto load_unit = [&](uint8_t* st, int op, int k0) {
