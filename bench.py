@@ -198,6 +198,29 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload:
     print("\n".join(lines))
 
 
+def host_description() -> str:
+    """CPU model and BLAS library of the host, for the oracle baseline."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown BLAS"
+    try:
+        from threadpoolctl import threadpool_info
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas = f"{p.get('internal_api', 'blas')} {p.get('version', '')}".strip()
+                break
+    except Exception:
+        pass
+    return f"{model}; {blas}"
+
+
 def cpu_baseline(w, inp, target_s: float):
     """The fp64 oracle, untuned, on a bounded row sample of the same workload."""
     import numpy as np
@@ -233,7 +256,8 @@ def cpu_baseline(w, inp, target_s: float):
     flops = 4.0 * rows * w.D * w.F
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"all {w.M} rows" if rows == w.M else f"first {rows} of {w.M} rows of X (rows are "
-                       "independent)") + f", D={w.D}, F={w.F}, n={w.n}; numpy fp64 oracle, {t:.1f} s"}
+                       "independent)") + f", D={w.D}, F={w.F}, n={w.n}; numpy fp64 oracle, {t:.1f} s; "
+                      + host_description()}
 
 
 BWD_METRIC = "TP-MLP backward TFLOP/s (8·M·D·F: dX, dA, dB), 1 MI355X"
@@ -349,7 +373,9 @@ def _timed_segments(args, step, nev, warm=True):
         step(evs[k])
     torch.cuda.synchronize()
     seg = [float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in evs])) for i in range(nev - 1)]
+    whole = [hip.elapsed_ms(e[0], e[nev - 1]) for e in evs]
     hip.close()
+    _timed_segments.step_stats = {"min": float(np.min(whole)), "median": float(np.median(whole))}
     return ms, seg
 
 
@@ -568,6 +594,7 @@ def main() -> int:
         "config": {"workload": w.name, "M": w.M, "D": w.D, "F": w.F, "n": w.n,
                    "layernorm": w.layernorm, "residual": w.residual, "layernorm_after": w.layernorm_after},
         "pct_of_peak": round(100.0 * value / peak, 2),
+        "step_ms_instrumented": {k: round(v, 5) for k, v in _timed_segments.step_stats.items()},
         "kernels_ms": {"ln_stats": round(float(np.mean(t_ln)), 5), "gemm1_gelu": round(g1, 5),
                        ("gemm2_sum_and_layernorm" if w.layernorm_after else "gemm2_sum"): round(g2, 5)},
         "roofline": roofline,
