@@ -270,12 +270,9 @@ hipError_t launch_rowsum(const void* x, int64_t rows, int64_t cols, int dtype, f
 }
 
 // ---------------------------------------------------------------------------
-// Strided transpose out[c][r] = f(in[r][c]) (r < R, c < C), with f the
-// identity (bit-exact) or the tanh GeLU ("Tensor-Parallel MLP (Megatron)",
-// section "GeLU").  Used to pack A (D x F) into K-contiguous A^T (F x D) and
-// B (F x D) into B^T (D x F), to unpack a shard, and in the backward to lay
-// the activations out with the batch axis contiguous (the weight gradients
-// contract over it).
+// Strided bit-exact transpose out[c][r] = in[r][c] (r < R, c < C).  Used to
+// pack A (D x F) into K-contiguous A^T (F x D) and B (F x D) into B^T (D x F),
+// to unpack a shard, and to pack the attention projections.
 //
 // Vector form: V = 16 / sizeof(T) elements per 16-byte chunk, a tile of 16V x
 // 16V elements per block of 256 threads.  Every global access is a 16-byte
@@ -288,21 +285,6 @@ hipError_t launch_rowsum(const void* x, int64_t rows, int64_t cols, int dtype, f
 // C, ldi, ldo to be multiples of V and 16-byte aligned pointers; other shapes
 // take the element-wise form below.
 // ---------------------------------------------------------------------------
-template <typename T, bool GELU>
-__device__ __forceinline__ u32x4 apply_chunk(u32x4 v) {
-    if constexpr (!GELU) {
-        return v;
-    } else {
-        constexpr int V = 16 / sizeof(T);
-        T vals[V];
-        __builtin_memcpy(vals, &v, 16);
-#pragma unroll
-        for (int e = 0; e < V; ++e) vals[e] = from_f32<T>(gelu_tanh(to_f32(vals[e])));
-        __builtin_memcpy(&v, vals, 16);
-        return v;
-    }
-}
-
 // x[i] holds row i of a V x V block as V elements packed in 4 dwords; y[c]
 // receives column c.  For 4-byte elements this is a renaming of dwords; for
 // 2-byte elements each output dword pairs the same half of two input dwords.
@@ -329,7 +311,7 @@ __device__ __forceinline__ void transpose_block<8>(const u32x4 (&x)[8], u32x4 (&
         }
 }
 
-template <typename T, bool GELU>
+template <typename T>
 __global__ __launch_bounds__(256) void transpose_vec_kernel(const T* __restrict__ in, int64_t ldi,
                                                             T* __restrict__ out, int64_t ldo, int64_t R,
                                                             int64_t C) {
@@ -347,7 +329,7 @@ __global__ __launch_bounds__(256) void transpose_vec_kernel(const T* __restrict_
         if (col_ok && r0 + row < R) {
             const u32x4 v = __builtin_nontemporal_load(
                 reinterpret_cast<const u32x4*>(in + (r0 + row) * ldi + c0 + (int64_t)ch * V));
-            tile[row * 16 + (ch ^ ((row / V) & 15))] = apply_chunk<T, GELU>(v);
+            tile[row * 16 + (ch ^ ((row / V) & 15))] = v;
         }
     }
     __syncthreads();
@@ -366,7 +348,7 @@ __global__ __launch_bounds__(256) void transpose_vec_kernel(const T* __restrict_
 
 // Element-wise form for any shape and alignment: a 64 x 64 tile, one element
 // per thread and access, LDS padded by one element per row.
-template <typename T, bool GELU>
+template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int64_t ldi,
                                                         T* __restrict__ out, int64_t ldo, int64_t R,
                                                         int64_t C) {
@@ -379,9 +361,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
     for (int i = 0; i < 16; ++i) {
         const int rr = ty + 4 * i;
         if (r0 + rr < R && c0 + tx < C) {
-            T v = in[(r0 + rr) * ldi + c0 + tx];
-            if constexpr (GELU) v = from_f32<T>(gelu_tanh(to_f32(v)));
-            tile[rr][tx] = v;
+            tile[rr][tx] = in[(r0 + rr) * ldi + c0 + tx];
         }
     }
     __syncthreads();
@@ -392,7 +372,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
     }
 }
 
-template <typename T, bool GELU>
+template <typename T>
 static hipError_t transpose_typed(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
                                   hipStream_t stream) {
     constexpr int64_t V = 16 / sizeof(T);
@@ -402,10 +382,10 @@ static hipError_t transpose_typed(const void* in, int64_t ldi, void* out, int64_
     T* dst = static_cast<T*>(out);
     if (vec) {
         const dim3 grid((unsigned)((C + 16 * V - 1) / (16 * V)), (unsigned)((R + 16 * V - 1) / (16 * V)));
-        transpose_vec_kernel<T, GELU><<<grid, dim3(256), 0, stream>>>(src, ldi, dst, ldo, R, C);
+        transpose_vec_kernel<T><<<grid, dim3(256), 0, stream>>>(src, ldi, dst, ldo, R, C);
     } else {
         const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-        transpose_kernel<T, GELU><<<grid, dim3(256), 0, stream>>>(src, ldi, dst, ldo, R, C);
+        transpose_kernel<T><<<grid, dim3(256), 0, stream>>>(src, ldi, dst, ldo, R, C);
     }
     return hipGetLastError();
 }
@@ -413,14 +393,8 @@ static hipError_t transpose_typed(const void* in, int64_t ldi, void* out, int64_
 hipError_t launch_transpose(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
                             int elem_bytes, hipStream_t stream) {
     // bit-exact copies: the element's type only sets its width
-    return elem_bytes == 4 ? transpose_typed<float, false>(in, ldi, out, ldo, R, C, stream)
-                           : transpose_typed<bf16, false>(in, ldi, out, ldo, R, C, stream);
-}
-
-hipError_t launch_transpose_gelu(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
-                                 int dtype, hipStream_t stream) {
-    return dtype == kF32 ? transpose_typed<float, true>(in, ldi, out, ldo, R, C, stream)
-                         : transpose_typed<bf16, true>(in, ldi, out, ldo, R, C, stream);
+    return elem_bytes == 4 ? transpose_typed<float>(in, ldi, out, ldo, R, C, stream)
+                           : transpose_typed<bf16>(in, ldi, out, ldo, R, C, stream);
 }
 
 }  // namespace tpmlp

@@ -73,7 +73,5 @@ hipError_t launch_attention(const void* qkv, int64_t ldq, const void* x, int64_t
 hipError_t launch_rowsum(const void* x, int64_t rows, int64_t cols, int dtype, float* out, hipStream_t stream);
 hipError_t launch_transpose(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
                             int elem_bytes, hipStream_t stream);
-hipError_t launch_transpose_gelu(const void* in, int64_t ldi, void* out, int64_t ldo, int64_t R, int64_t C,
-                                 int dtype, hipStream_t stream);
 
 }  // namespace tpmlp
