@@ -71,8 +71,11 @@ template <int WB> struct Tile {
 };
 
 // The GeLU epilogue that also stores the pre-activation (GemmArgs::preact_out
-// set): its own instantiation, so the plain GeLU epilogue carries none of it.
+// set), and the GeLU-derivative epilogue that also stores GeLU of its operand
+// (GemmArgs::gelu_out set): their own instantiations, so the plain epilogues
+// carry none of it.
 constexpr int kEpiGeluSave = 3;
+constexpr int kEpiGeluGradSave = 4;
 
 struct FastParams {
     const bf16* A;
@@ -90,6 +93,7 @@ struct FastParams {
     const bf16* aux;     // kEpiGeluGrad: pre-activation, M x N
     int64_t ldaux;
     bf16* preact;        // kEpiGelu: optional copy of the pre-activation (C's layout)
+    bf16* gelu_out;      // kEpiGeluGrad: optional GeLU of the pre-activation (C's layout)
     int tiles_m, tiles_n;
     int group;           // tile rows walked together on one XCD
     int nt_store;        // write C with non-temporal stores
@@ -444,9 +448,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // The epilogue's operand (the pre-activation, or the residual) is read
     // for the whole wave tile before the first row block is transformed, so
     // its memory latency is paid once rather than once per row block.
-    constexpr bool kHasAux = EPI == kEpiGeluGrad || EPI == kEpiStore;
+    constexpr bool kGrad = EPI == kEpiGeluGrad || EPI == kEpiGeluGradSave;
+    constexpr bool kHasAux = kGrad || EPI == kEpiStore;
     bf16x4 ex[kHasAux ? NB : 1][kHasAux ? NB : 1];
-    if constexpr (EPI == kEpiGeluGrad) {
+    if constexpr (kGrad) {
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -491,7 +496,20 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
                 }
             }
             gelu_tanh_staged(v);
-        } else if constexpr (EPI == kEpiGeluGrad) {
+        } else if constexpr (kGrad) {
+            if constexpr (EPI == kEpiGeluGradSave) {
+                // GeLU of the pre-activation (the forward's H), for the
+                // gradient of the second weight
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(gelu_tanh(static_cast<float>(ex[i][j][r])));
+                    bf16x4* dst = reinterpret_cast<bf16x4*>(p.gelu_out + m * p.ldc + n_base + j * 16);
+                    if (p.nt_store) __builtin_nontemporal_store(o, dst);
+                    else *dst = o;
+                }
+            }
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -539,6 +557,7 @@ hipError_t launch_typed(const GemmArgs& g, int splits, hipStream_t stream) {
     p.mean = g.ln_mean; p.rstd = g.ln_rstd; p.csum = g.ln_csum;
     p.aux = static_cast<const bf16*>(g.aux); p.ldaux = g.ldaux;
     p.preact = static_cast<bf16*>(g.preact_out);
+    p.gelu_out = static_cast<bf16*>(g.gelu_out);
     p.tiles_m = (int)(g.M / BM);
     p.tiles_n = (int)(g.N / BN);
     p.group = 4;
@@ -576,7 +595,8 @@ static int device_cus() {
 // 64-wide steps, 16-byte aligned rows, one operand tile's byte offsets below 2^31
 // (buffer offsets), and, with the LayerNorm epilogue, the column sums of Bop.
 // K-major operands: Bop alone (store or GeLU-derivative epilogue) or both
-// (store epilogue), without LayerNorm or the pre-activation stash.
+// (store epilogue), without LayerNorm or the pre-activation stash.  The
+// GeLU output of the GeLU-derivative epilogue goes with that epilogue only.
 static bool fits_tile(const GemmArgs& g, int wb) {
     const int64_t tm = 64 * wb;
     if (g.ab_dtype != kBF16) return false;
@@ -602,6 +622,7 @@ static bool fits_tile(const GemmArgs& g, int wb) {
                                   g.c_dtype != kBF16))
         return false;
     if (g.preact_out && (reinterpret_cast<uintptr_t>(g.preact_out) & 7)) return false;
+    if (g.gelu_out && (g.epi != kEpiGeluGrad || (reinterpret_cast<uintptr_t>(g.gelu_out) & 7))) return false;
     return true;
 }
 
@@ -709,13 +730,17 @@ static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
     // GeLU-derivative epilogue and no LayerNorm)
     if (g.a_kmajor && g.b_kmajor) return launch_store<WB, 3>(g, stream);
     if (g.b_kmajor) {
-        if (g.epi == kEpiGeluGrad) return launch_typed<WB, kEpiGeluGrad, bf16, 2>(g, 1, stream);
+        if (g.epi == kEpiGeluGrad)
+            return g.gelu_out ? launch_typed<WB, kEpiGeluGradSave, bf16, 2>(g, 1, stream)
+                              : launch_typed<WB, kEpiGeluGrad, bf16, 2>(g, 1, stream);
         return launch_store<WB, 2>(g, stream);
     }
     if (g.epi == kEpiGelu)
         return g.preact_out ? launch_typed<WB, kEpiGeluSave, bf16>(g, 1, stream)
                             : launch_typed<WB, kEpiGelu, bf16>(g, 1, stream);
-    if (g.epi == kEpiGeluGrad) return launch_typed<WB, kEpiGeluGrad, bf16>(g, 1, stream);
+    if (g.epi == kEpiGeluGrad)
+        return g.gelu_out ? launch_typed<WB, kEpiGeluGradSave, bf16>(g, 1, stream)
+                          : launch_typed<WB, kEpiGeluGrad, bf16>(g, 1, stream);
     return launch_store<WB, 0>(g, stream);
 }
 

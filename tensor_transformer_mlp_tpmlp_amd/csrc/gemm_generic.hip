@@ -35,6 +35,7 @@ struct GenericParams {
     const void* aux;     // kEpiGeluGrad: pre-activation, operand dtype
     int64_t ldaux;
     void* preact;        // kEpiGelu: optional copy of the pre-activation (C's layout and dtype)
+    void* gelu_out;      // kEpiGeluGrad: optional GeLU of the pre-activation (C's layout and dtype)
     int64_t tiles_n;
     int a_km, b_km;      // operand stored K-major (see GemmArgs)
 };
@@ -116,7 +117,9 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GenericParams p) {
                 if (p.preact) static_cast<TC*>(p.preact)[m * p.ldc + n] = from_f32<TC>(v);
                 v = gelu_tanh(v);
             } else if constexpr (EPI == kEpiGeluGrad) {
-                v *= gelu_tanh_grad(to_f32(static_cast<const T*>(p.aux)[m * p.ldaux + n]));
+                const float s = to_f32(static_cast<const T*>(p.aux)[m * p.ldaux + n]);
+                if (p.gelu_out) static_cast<TC*>(p.gelu_out)[m * p.ldc + n] = from_f32<TC>(gelu_tanh(s));
+                v *= gelu_tanh_grad(s);
             } else {
                 if (R) v += to_f32(R[m * p.ldr + n]);
             }
@@ -134,6 +137,7 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t stream) {
     p.mean = g.ln_mean; p.rstd = g.ln_rstd;
     p.aux = g.aux; p.ldaux = g.ldaux;
     p.preact = g.preact_out;
+    p.gelu_out = g.gelu_out;
     p.tiles_n = (g.N + GT - 1) / GT;
     p.a_km = g.a_kmajor ? 1 : 0;
     p.b_km = g.b_kmajor ? 1 : 0;

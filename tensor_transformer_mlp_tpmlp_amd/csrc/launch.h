@@ -38,6 +38,7 @@ struct GemmArgs {
     const void* aux = nullptr;  // kEpiGeluGrad: the pre-activation, M x N (ldaux)
     int64_t ldaux = 0;
     void* preact_out = nullptr;  // kEpiGelu: also store the pre-activation here (M x N, ldc, C's dtype)
+    void* gelu_out = nullptr;    // kEpiGeluGrad: also store GeLU_tanh(aux) here (M x N, ldc, C's dtype)
     // Split-K scratch (fp32 partial sums); gemm_split_bytes(g) bytes.  Only
     // a GEMM that would leave most of the GPU idle (few output tiles, long
     // K, a plain store epilogue) is split; the others ignore it.

@@ -119,6 +119,7 @@ GemmArgs bwd_args(const tpmlp_shards* s, int64_t M, int which, const BwdPtrs& q)
             g.A = q.dY; g.lda = D; g.B = q.bt; g.ldb = F; g.b_kmajor = true;
             g.M = M; g.N = F; g.K = D; g.C = q.dS; g.ldc = F;
             g.epi = kEpiGeluGrad; g.aux = q.S; g.ldaux = F;
+            g.gelu_out = q.H;
             break;
         case kBwdDX:
             g.A = q.dS; g.lda = F; g.B = q.at; g.ldb = D; g.b_kmajor = true;
@@ -445,10 +446,10 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
     };
 
     hipError_t e = hipSuccess;
-    // S = X A for all shards at once, unless the forward kept it; H = GeLU(S)
+    // S = X A for all shards at once, unless the forward kept it
     if (!preact) e = gemm(kBwdS);
-    if (e == hipSuccess) e = launch_gelu(q.S, q.H, M * F, dt, hs);
-    // dS = (dY B^T) * GeLU'(S): the gradient at every shard's GeLU input
+    // dS = (dY B^T) * GeLU'(S), the gradient at every shard's GeLU input; the
+    // epilogue that reads S also writes H = GeLU(S) for dB
     if (e == hipSuccess) e = gemm(kBwdDS);
     // dX = sum_i dS_i A_i^T: the K loop over F sums the shards in registers
     if (e == hipSuccess) e = gemm(kBwdDX);
