@@ -50,6 +50,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 namespace tpmlp {
@@ -626,12 +627,24 @@ static bool fits_tile(const GemmArgs& g, int wb) {
     return true;
 }
 
-// 256x256 tiles (wb = 4) when they keep at least 3/4 of the CUs busy, else
-// 128x128 tiles (wb = 2, two workgroups per CU); 0 = not for the MFMA kernel.
+// Tile size: 256x256 (wb = 4, one workgroup per CU) or 128x128 (wb = 2, two
+// per CU); 0 = not for the MFMA kernel.  With t 256x256 tiles on C CUs, the
+// 256x256 plan takes ceil(t / C) rounds, a partial round lasting as long as
+// a full one.  A round of 128x128 tiles does half the work of a 256x256
+// round in 0.515 of its time (measured at K = 1024 on MI355X) and, its tiles
+// being finer, a partial round costs about its share: 0.515 * 4 t / (2 C).
+// The cheaper plan wins; 256x256 on a tie (its L2 reuse is better).
 static int choose_wb(const GemmArgs& g) {
-    if (fits_tile(g, 4) && (g.M / 256) * (g.N / 256) * 4 >= 3 * (int64_t)device_cus()) return 4;
-    if (fits_tile(g, 2)) return 2;
-    if (fits_tile(g, 4)) return 4;
+    const bool f4 = fits_tile(g, 4), f2 = fits_tile(g, 2);
+    if (f4 && f2) {
+        const double cus = (double)device_cus();
+        const double t4 = (double)(g.M / 256) * (double)(g.N / 256);
+        const double rounds4 = std::ceil(t4 / cus);
+        const double rounds2 = 0.515 * 4.0 * t4 / (2.0 * cus);
+        return rounds2 < rounds4 ? 2 : 4;
+    }
+    if (f2) return 2;
+    if (f4) return 4;
     return 0;
 }
 
