@@ -74,6 +74,27 @@ class HipEvents:
         self.events = []
 
 
+def device_info() -> dict:
+    """The GPU of the run: name, CU count and peak shader clock (HIP's
+    hipDeviceAttributeClockRate, attribute 5, in kHz), and the dense bf16
+    MFMA peak they give at 4096 FLOP per clock per CU (the 2516.6 TFLOP/s
+    figure is 256 CUs at 2.4 GHz).  The clock the GEMMs sustain under load is
+    lower; the counter profile of the headline GEMMs measures it."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int()
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) == 0 and khz.value > 0:
+            ghz = khz.value / 1e6
+            info["peak_clock_ghz"] = round(ghz, 3)
+            info["bf16_peak_tflops_from_cus_and_clock"] = round(props.multi_processor_count * 4096 * ghz / 1e3, 1)
+    except OSError:
+        pass
+    return info
+
+
 def _sha256(path: str) -> str:
     with open(os.path.join(ROOT, path), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -598,6 +619,7 @@ def main() -> int:
         "kernels_ms": {"ln_stats": round(float(np.mean(t_ln)), 5), "gemm1_gelu": round(g1, 5),
                        ("gemm2_sum_and_layernorm" if w.layernorm_after else "gemm2_sum"): round(g2, 5)},
         "roofline": roofline,
+        "device": device_info(),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
