@@ -10,10 +10,10 @@ block_s{128,256,512}_bf16 (the whole block with the time of each half).
 One step is one full forward of the hot path, Y = sum_i GeLU_tanh(X A_i) B_i
 (plus LayerNorm and the residual for the Post-LN workloads), over inputs
 already resident in HBM.  Weights are packed before timing (they are static).
-Prints ONE JSON line: whole-forward TFLOP/s (4*M*D*F per step, from a timed
-loop with no events inside it), the roofline of the dominant kernel from HIP
-events recorded around each kernel in a second pass of the same steps, and
-the fp64 oracle timed on the host cores on a row sample.
+Prints ONE JSON line: whole-forward TFLOP/s (4*M*D*F per step, from the timed
+loop), the roofline of the dominant kernel from HIP events recorded around
+each kernel on a sample of the timed steps (live, inside the timed
+region), and the fp64 oracle timed on the host cores on a row sample.
 """
 
 from __future__ import annotations
@@ -368,35 +368,38 @@ BLOCK_METRIC = "block forward ms per step (attention half + FFN half), 1 MI355X"
 
 
 def _timed_segments(args, step, nev, warm=True):
-    """Warm up, time args.steps calls of step(None) between two events on the
-    stream (the per-step time: nothing else is recorded inside the loop),
-    then run the same number of steps again with nev HIP events per call
-    around the kernels (each record costs a few microseconds of queue time,
-    which is why it stays out of the first loop).  Returns (ms per step,
-    [mean ms of each of the nev - 1 intervals])."""
+    """Warm up, then time args.steps calls of step(events) between two events
+    on the stream.  One timed step in `every` (every = max(4, steps / 10),
+    so about ten samples) also records nev HIP events around its kernels
+    (the library's event argument), so the per-kernel intervals are measured
+    live, inside the timed region; the other steps pass none, which keeps
+    the records' few microseconds of queue time out of most steps (it
+    matters only for steps of tens of microseconds).  Returns (ms per step,
+    [mean ms of each of the nev - 1 intervals over the sampled steps])."""
     import numpy as np
     import torch
+
+    every = max(4, args.steps // 10)
 
     if warm:
         for _ in range(args.warmup):
             step(None)
     torch.cuda.synchronize()
+    hip = HipEvents()
+    sampled = [k for k in range(args.steps) if k % every == every - 1] or [args.steps - 1]
+    evs = {k: [hip.create() for _ in range(nev)] for k in sampled}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps):
-        step(None)
+    for k in range(args.steps):
+        step(evs.get(k))
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    hip = HipEvents()
-    evs = [[hip.create() for _ in range(nev)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    seg = [float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in evs])) for i in range(nev - 1)]
-    whole = [hip.elapsed_ms(e[0], e[nev - 1]) for e in evs]
+    seg = [float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in evs.values()])) for i in range(nev - 1)]
+    whole = [hip.elapsed_ms(e[0], e[nev - 1]) for e in evs.values()]
     hip.close()
-    _timed_segments.step_stats = {"min": float(np.min(whole)), "median": float(np.median(whole))}
+    _timed_segments.step_stats = {"min": float(np.min(whole)), "median": float(np.median(whole)),
+                                  "sampled_steps": len(whole)}
     return ms, seg
 
 
