@@ -553,7 +553,7 @@ def main() -> int:
 
     if args.gpus != 1:
         msg = (f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-               "(the multi-GPU all-reduce is not part of this build)")
+               "(the multi-GPU all-reduce is not implemented; the one-GPU path sums the shards on-chip)")
         print(msg, file=sys.stderr)
         print(json.dumps({"error": msg, "n_gpus": args.gpus}))
         return 2
