@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import List, Optional, Sequence, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
@@ -125,6 +125,24 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+class _StreamWorkspaces:
+    """Grow-only device workspaces, one per stream.  Calls on one stream run
+    in order and can share a workspace; calls on different streams may
+    overlap, so each stream gets its own."""
+
+    def __init__(self, device: torch.device):
+        self.device = device
+        self._by_stream: Dict[int, torch.Tensor] = {}
+
+    def get(self, nbytes: int, stream: int) -> torch.Tensor:
+        ws = self._by_stream.get(stream)
+        if ws is None or ws.numel() < nbytes:
+            # allocated on the current stream, which is `stream`
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self._by_stream[stream] = ws
+        return ws
+
+
 def gelu(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Elementwise tanh-GeLU on the GPU (tpmlp_gelu)."""
     if out is None:
@@ -140,7 +158,7 @@ class Shards:
     """n (A_i, B_i) pairs packed on the GPU (a tpmlp_shards descriptor).
 
     Holds the packed weight buffer (owned here, as a torch tensor) and a
-    grow-only forward workspace.
+    grow-only workspace per stream.
     """
 
     def __init__(self, handle: int, packed: torch.Tensor, D: int, F: int, n: int, dtype: torch.dtype):
@@ -148,7 +166,7 @@ class Shards:
         self.packed = packed
         self.D, self.F, self.n, self.dtype = D, F, n, dtype
         self.device = packed.device
-        self._ws: Optional[torch.Tensor] = None
+        self._ws = _StreamWorkspaces(self.device)
 
     @property
     def handle(self) -> int:
@@ -169,10 +187,8 @@ class Shards:
             out.append((A_i, B_i))
         return out
 
-    def workspace(self, nbytes: int) -> torch.Tensor:
-        if self._ws is None or self._ws.numel() < nbytes:
-            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
-        return self._ws
+    def workspace(self, nbytes: int, stream: int) -> torch.Tensor:
+        return self._ws.get(nbytes, stream)
 
     def close(self) -> None:
         if self._handle:
@@ -233,7 +249,8 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, layernor
     flags = (OPT_LAYERNORM if layernorm else 0) | (OPT_LAYERNORM_AFTER if layernorm_after else 0)
     L = lib()
     nbytes = L.tpmlp_forward_workspace_bytes(shards.handle, M, flags, 1 if shard_index >= 0 else 0)
-    ws = shards.workspace(nbytes)
+    stream = _stream(X.device)
+    ws = shards.workspace(nbytes, stream)
     o = Opts()
     L.tpmlp_opts_init(ctypes.byref(o))
     o.flags = flags
@@ -256,8 +273,8 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, layernor
         ev_arr = (ctypes.c_void_p * 4)(*[e or None for e in events])
         o.events = ctypes.cast(ev_arr, ctypes.c_void_p)
     _check(L.tpmlp_forward_ex(_dev(X, "X") if M else X.data_ptr(), M, shards.handle,
-                              _dev(out, "out") if M else out.data_ptr(), ctypes.byref(o),
-                              _stream(X.device)), "tpmlp_forward_ex")
+                              _dev(out, "out") if M else out.data_ptr(), ctypes.byref(o), stream),
+           "tpmlp_forward_ex")
     return out
 
 
@@ -293,10 +310,11 @@ def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards, out=None,
         pp = _dev(preact, "preact") if M else None
     L = lib()
     nbytes = L.tpmlp_backward_workspace_bytes(shards.handle, M)
-    ws = shards.workspace(nbytes)
+    stream = _stream(X.device)
+    ws = shards.workspace(nbytes, stream)
     _check(L.tpmlp_backward(_dev(X, "X") if M else X.data_ptr(), _dev(dY, "dY") if M else dY.data_ptr(), M,
                             shards.handle, pp, _dev(dX, "dX") if M else dX.data_ptr(), _dev(dA, "dA"),
-                            _dev(dB, "dB"), ws.data_ptr(), ws.numel(), _stream(X.device)), "tpmlp_backward")
+                            _dev(dB, "dB"), ws.data_ptr(), ws.numel(), stream), "tpmlp_backward")
     return dX, dA, dB
 
 
@@ -304,7 +322,7 @@ class AttnWeights:
     """Packed projection weights of the attention half (a tpmlp_attn descriptor).
 
     Holds the packed buffer (owned here, as a torch tensor) and a grow-only
-    workspace.
+    workspace per stream.
     """
 
     def __init__(self, handle: int, packed: torch.Tensor, hidden: int, heads: int, p: int, has_wo: bool):
@@ -312,16 +330,14 @@ class AttnWeights:
         self.packed = packed
         self.hidden, self.heads, self.p, self.has_wo = hidden, heads, p, has_wo
         self.device = packed.device
-        self._ws: Optional[torch.Tensor] = None
+        self._ws = _StreamWorkspaces(self.device)
 
     @property
     def handle(self) -> int:
         return self._handle
 
-    def workspace(self, nbytes: int) -> torch.Tensor:
-        if self._ws is None or self._ws.numel() < nbytes:
-            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
-        return self._ws
+    def workspace(self, nbytes: int, stream: int) -> torch.Tensor:
+        return self._ws.get(nbytes, stream)
 
     def close(self) -> None:
         if self._handle:
@@ -370,7 +386,8 @@ def attention(x: torch.Tensor, batch: int, seq: int, weights: AttnWeights, *, la
     elif out.dtype != x.dtype or out.shape != x.shape:
         raise ValueError("out must match x")
     L = lib()
-    ws = weights.workspace(L.tpmlp_attn_workspace_bytes(weights.handle, batch, seq))
+    stream = _stream(x.device)
+    ws = weights.workspace(L.tpmlp_attn_workspace_bytes(weights.handle, batch, seq), stream)
     flags = (ATTN_LAYERNORM if layernorm else 0) | (ATTN_RESIDUAL if residual else 0)
     M = batch * seq
     ev_arr = None
@@ -378,6 +395,6 @@ def attention(x: torch.Tensor, batch: int, seq: int, weights: AttnWeights, *, la
         ev_arr = (ctypes.c_void_p * 4)(*[e or None for e in events])
     _check(L.tpmlp_attention(_dev(x, "x") if M else x.data_ptr(), batch, seq, weights.handle,
                              _dev(out, "out") if M else out.data_ptr(), flags, eps, ws.data_ptr(), ws.numel(),
-                             ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
-                             _stream(x.device)), "tpmlp_attention")
+                             ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None, stream),
+           "tpmlp_attention")
     return out

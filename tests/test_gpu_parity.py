@@ -294,7 +294,8 @@ def test_determinism_and_every_tile_written():
     X, A, B = (to_dev(a, torch.bfloat16) for a in (inp.X, inp.A, inp.B))
     sh = tp.shard_mlp(A, B, w.n)
     y1 = torch.full((w.M, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
-    ws = sh.workspace(tp.lib().tpmlp_forward_workspace_bytes(sh.handle, w.M, 0, 0))
+    stream = torch.cuda.current_stream().cuda_stream
+    ws = sh.workspace(tp.lib().tpmlp_forward_workspace_bytes(sh.handle, w.M, 0, 0), stream)
     ws.fill_(0xFF)  # NaN bit patterns in H
     tp.tp_mlp(X, sh, out=y1)
     y2 = torch.full_like(y1, float("nan"))
@@ -302,6 +303,32 @@ def test_determinism_and_every_tile_written():
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y1).all())
     assert torch.equal(y1, y2)
+
+
+def test_two_streams_at_once_share_no_workspace():
+    """One descriptor used by forwards on two streams at the same time: the
+    binding gives each stream its own workspace (H), so each result equals
+    its sequential one bit for bit."""
+    say("two streams, one descriptor, concurrent forwards")
+    M, D, F, n = 1024, 512, 2048, 4
+    inp1 = workloads.random_case(M, D, F, seed=91, dtype="bf16")
+    inp2 = workloads.random_case(M, D, F, seed=92, dtype="bf16")
+    dt = torch.bfloat16
+    A, B = to_dev(inp1.A, dt), to_dev(inp1.B, dt)
+    X1, X2 = to_dev(inp1.X, dt), to_dev(inp2.X, dt)
+    sh = tp.shard_mlp(A, B, n)
+    ref1, ref2 = tp.tp_mlp(X1, sh), tp.tp_mlp(X2, sh)
+    Y1, Y2 = torch.empty_like(ref1), torch.empty_like(ref2)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(8):
+        with torch.cuda.stream(s1):
+            tp.tp_mlp(X1, sh, out=Y1)
+        with torch.cuda.stream(s2):
+            tp.tp_mlp(X2, sh, out=Y2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, ref1)
+    assert torch.equal(Y2, ref2)
 
 
 def test_empty_and_single_row():
