@@ -580,7 +580,7 @@ hipError_t launch_typed(const GemmArgs& g, int splits, hipStream_t stream) {
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // CUs of the current device (queried once; 256 on MI355X).
-static int device_cus() {
+int device_cu_count() {
     static int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -590,6 +590,7 @@ static int device_cus() {
     }();
     return cus;
 }
+static int device_cus() { return device_cu_count(); }
 
 // Whether the MFMA kernel can take a shape with tiles of 64*wb rows: bf16
 // operands, M and N whole tiles, K a whole number (at least three) of

@@ -58,6 +58,9 @@ enum GemmPath { kPathFastBf16 = 0, kPathGeneric = 1 };
 GemmPath choose_gemm_path(const GemmArgs& g);
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+
+// Compute units of the current device (queried once).
+int device_cu_count();
 hipError_t launch_gemm_generic(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_bf16_fast(const GemmArgs& g, hipStream_t stream);
 
