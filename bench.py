@@ -544,6 +544,8 @@ def main() -> int:
     ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
                     help="time the forward (default, the headline metric) or the backward pass")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
 
     if args.summarize_profiles:
         import workloads
