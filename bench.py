@@ -493,24 +493,10 @@ def bench_block(args, s: int) -> int:
     aw = tp.shard_attention(bf(ai.Wq), bf(ai.Wk), bf(ai.Wv), wa.heads, wa.p)
     shards = tp.shard_mlp(bf(fi.A), bf(fi.B), wf.n)
     x1, y = torch.empty_like(x), torch.empty_like(x)
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev).cuda_stream
-
-    def record(e):
-        if hip.hipEventRecord(e, stream) != 0:
-            raise RuntimeError("hipEventRecord failed")
 
     def step(ev):
-        if ev:
-            record(ev[0])
-        tp.attention(x, wa.batch, wa.seq, aw, out=x1)
-        if ev:
-            record(ev[1])
-        tp.tp_mlp(x1, shards, layernorm=True, residual=x1, out=y)
-        if ev:
-            record(ev[2])
+        tp.block(x, wa.batch, wa.seq, aw, shards, x1=x1, out=y, events=ev)
 
     ms, (t_attn, t_ffn) = _timed_segments(args, step, 3)
     log(f"[bench] block s={s}: {ms:.4f} ms/step (attention {t_attn:.4f}, FFN {t_ffn:.4f})")

@@ -17,6 +17,7 @@ from .tpmlp import (  # noqa: F401
     Shards,
     TpmlpError,
     attention,
+    block,
     gelu,
     lib,
     shard_attention,

@@ -267,10 +267,13 @@ constexpr int kTileB = kKT * kRowB;  // 8 KiB: one K tile or one V tile
 // 16 w .. 16 w + 15 of each tile in two loads of 8 rows; lane L lands at row
 // 16 w + 8 q + L/8, physical chunk L % 8, so it reads the logical chunk
 // (L % 8) ^ swizzle(row) of that row.  Buffer resources cover this
-// sequence's rows (plus one tile) up to the end of QKV: rows past the last
-// token read as zero, and rows of the next sequence are masked (keys) or
-// multiplied by P = 0 (values) like any row past the sequence end.  Requires
-// (seq + 64) rows of QKV below 2 GiB (buffer offsets).
+// sequence's rows (plus one tile) up to the end of QKV, and each load's
+// whole byte offset, the tile's first row included, is a per-lane (VGPR)
+// offset with a zero scalar offset: the hardware's range check covers only
+// the per-lane offset, so this is what makes rows past the end of QKV read
+// as zero.  Rows of the next sequence are masked (keys) or multiplied by
+// P = 0 (values) like any row past the sequence end.  Requires (seq + 64)
+// rows of QKV below 2 GiB (buffer offsets).
 template <int QB>
 __global__ __launch_bounds__(256) void attn_fwd_ring_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][2][kTileB];
@@ -307,10 +310,10 @@ __global__ __launch_bounds__(256) void attn_fwd_ring_kernel(AttnParams p) {
 
     auto issue = [&](int kv0, int st) {
         const uint32_t so = (uint32_t)(kv0 * p.ldq * 2);
-        dma16_asm(&ring[st][0][dst0], rk, kv_0, so);
-        dma16_asm(&ring[st][0][dst1], rk, kv_1, so);
-        dma16_asm(&ring[st][1][dst0], rv, vv_0, so);
-        dma16_asm(&ring[st][1][dst1], rv, vv_1, so);
+        dma16_asm(&ring[st][0][dst0], rk, kv_0 + so, 0u);
+        dma16_asm(&ring[st][0][dst1], rk, kv_1 + so, 0u);
+        dma16_asm(&ring[st][1][dst0], rv, vv_0 + so, 0u);
+        dma16_asm(&ring[st][1][dst1], rv, vv_1 + so, 0u);
     };
 
     f32x4 o[QB][4], ls[QB];

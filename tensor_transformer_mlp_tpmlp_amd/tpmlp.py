@@ -398,3 +398,24 @@ def attention(x: torch.Tensor, batch: int, seq: int, weights: AttnWeights, *, la
                              ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None, stream),
            "tpmlp_attention")
     return out
+
+
+def block(x: torch.Tensor, batch: int, seq: int, weights: AttnWeights, shards: Shards, *, eps: float = 1e-5,
+          x1: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+          events: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """The whole block forward in the code order of "LLM Lab Notes 06",
+    section 2, markers 2 to 7: x1 = x + attn(LayerNorm(x)) (tpmlp_attention),
+    then out = x1 + TP-MLP(LayerNorm(x1)) (tpmlp_forward_ex).  Two library
+    calls on the current stream; x1 (optional) receives the attention half's
+    output.  events: three hipEvent_t handles recorded before the attention
+    half, between the halves and after the FFN half (segment timing)."""
+    if shards.D != weights.hidden or shards.dtype != x.dtype:
+        raise ValueError("the FFN weights must have the attention's hidden size and x's dtype")
+    if x1 is None:
+        x1 = torch.empty_like(x)
+    ev = list(events) if events is not None else [None, None, None]
+    if len(ev) != 3:
+        raise ValueError("events must hold three handles")
+    attention(x, batch, seq, weights, layernorm=True, residual=True, eps=eps, out=x1,
+              events=[ev[0], None, None, ev[1]])
+    return tp_mlp(x1, shards, layernorm=True, eps=eps, residual=x1, out=out, events=[None, None, None, ev[2]])

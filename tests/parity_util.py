@@ -73,4 +73,14 @@ def sample_rows(M: int, count: int, seed: int) -> np.ndarray:
     return np.array(sorted(rows), dtype=np.int64)
 
 
+def sample_rows_per_tile(M: int, tile: int, seed: int) -> np.ndarray:
+    """One seeded row from every `tile`-row block of M rows (the last block
+    may be partial), plus the first and last rows."""
+    rng = np.random.default_rng(seed)
+    rows = {0, M - 1}
+    for t0 in range(0, M, tile):
+        rows.add(int(t0 + rng.integers(0, min(tile, M - t0))))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
 __all__ = ["workloads", "oracle"]

@@ -154,3 +154,36 @@ def test_attention_empty_and_errors():
         tp.shard_attention(Wq, Wk, Wv, 2, 3)              # p does not divide heads
     with pytest.raises(tp.TpmlpError):
         tp.shard_attention(*(W.float() for W in (Wq, Wk, Wv)), 2, 2)  # fp32 weights
+
+
+def test_attention_ragged_last_sequence_reads_nothing_past_qkv():
+    """The last sequence's last key tile is partial (s = 100: rows 64..127
+    of a 100-row sequence).  Rows past the end of Q|K|V must read as zero,
+    not as whatever follows it.  Without W^O and on the ragged-M projection
+    path (no split scratch) Q|K|V is the last workspace segment; the
+    workspace here is one key tile longer than asked for, and that tail
+    (like all of it) starts as 0xFF bytes, NaN in bf16.  A value row read
+    from there would put NaN into every query row of its head (P = 0 times
+    NaN), so the output must be finite and match the oracle."""
+    batch, seq, heads, p = 2, 100, 4, 2
+    h = 64 * heads
+    say(f"attention ragged last sequence b={batch} s={seq} H={heads}, NaN tail after Q|K|V")
+    inp = workloads.attn_case(batch, seq, h, seed=808, sw=1.0 / np.sqrt(h))
+    x, Wq, Wk, Wv, _ = _dev_inputs(inp)
+    aw = tp.shard_attention(Wq, Wk, Wv, heads, p)
+    L = tp.lib()
+    nbytes = L.tpmlp_attn_workspace_bytes(aw.handle, batch, seq)
+    tail = 64 * 3 * h * 2
+    ws = torch.full((nbytes + tail,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream().cuda_stream
+    for flags in (0, 3):
+        st = L.tpmlp_attention(x.data_ptr(), batch, seq, aw.handle, out.data_ptr(), flags, 0.0, ws.data_ptr(),
+                               nbytes, None, stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        # the tail was not written
+        assert bool((ws[nbytes:] == 0xFF).all())
+        ref = ao.attention_half(inp.x, inp.Wq, inp.Wk, inp.Wv, heads, p, batch, seq,
+                                layernorm=bool(flags & 1), residual=bool(flags & 2))
+        assert_close(to_f64(out), ref, "bf16", f"ragged last sequence, flags={flags}")

@@ -13,8 +13,8 @@ import torch
 import oracle
 import workloads
 import tensor_transformer_mlp_tpmlp_amd as tp
-from parity_util import (TOL_BF16, TOL_F32, assert_close, oracle_forward, sample_rows, say, to_dev,
-                         to_f64, torch_dtype)
+from parity_util import (TOL_BF16, TOL_F32, assert_close, oracle_forward, sample_rows, sample_rows_per_tile,
+                         say, to_dev, to_f64, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -188,15 +188,29 @@ def test_workload_h1024_full():
 
 @pytest.mark.parametrize("name", ["mlp_h4096_bf16", "rank_h8192_bf16"])
 def test_workload_large_sampled_rows(name):
+    """The full-size workloads, with Y and the whole workspace (H) filled
+    with NaN before the forward: every element of Y must then be finite
+    (every output tile written, no stale H read), and one seeded row of
+    every 256-row tile, plus the first and last rows, is compared with the
+    oracle (rows of Y depend only on the same rows of X)."""
     w = workloads.WORKLOADS[name]
-    say(f"{w.name}: {w.note} (sampled rows)")
+    say(f"{w.name}: {w.note} (NaN-poisoned Y and workspace, a row of every 256-row tile)")
     inp = workloads.make_inputs(w)
-    Y, _, _ = _run(inp, w.n, "bf16")
-    rows = sample_rows(w.M, 40, seed=w.seed)
+    dt = torch.bfloat16
+    X, A, B = to_dev(inp.X, dt), to_dev(inp.A, dt), to_dev(inp.B, dt)
+    sh = tp.shard_mlp(A, B, w.n)
+    stream = torch.cuda.current_stream().cuda_stream
+    ws = sh.workspace(tp.lib().tpmlp_forward_workspace_bytes(sh.handle, w.M, 0, 0), stream)
+    ws.fill_(0xFF)  # NaN bit patterns everywhere in the workspace
+    Y = torch.full((w.M, w.D), float("nan"), dtype=dt, device="cuda")
+    tp.tp_mlp(X, sh, out=Y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Y).all()), "an element of Y was not written (or read a NaN)"
+    rows = sample_rows_per_tile(w.M, 256, seed=w.seed)
+    assert len(rows) >= w.M // 256
     got = to_f64(Y[torch.from_numpy(rows).to(Y.device)])
     ref = oracle_forward(inp.X[rows], inp.A, inp.B, w.n)
     assert_close(got, ref, "bf16", f"{w.name} rows {len(rows)}")
-    assert bool(torch.isfinite(Y).all())
 
 
 def test_wide_output_residual_fp32_sampled_rows():
