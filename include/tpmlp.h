@@ -214,6 +214,33 @@ void tpmlp_opts_init(tpmlp_opts* o);
 tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, void* Y,
                               const tpmlp_opts* opts, void* stream);
 
+/* Size of the library's own per-device scratch array used by
+ * tpmlp_forward_noalloc: 64 MiB. */
+#define TPMLP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * tpmlp_forward_noalloc -- tpmlp_forward_ex for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It computes exactly what
+ * tpmlp_forward_ex computes with the same arguments, with the same kernels,
+ * but its workspace is a fixed array of TPMLP_NOALLOC_SCRATCH_BYTES in the
+ * library's device memory (one per GPU, held until the process ends), so
+ * neither the caller nor the library allocates anything.  The caller still
+ * passes X, Y (and any residual or save_preact buffer).
+ *   opts  as for tpmlp_forward_ex (NULL for the defaults); opts->workspace
+ *         must be NULL (TPMLP_ERR_WORKSPACE otherwise).
+ * A forward whose workspace (tpmlp_forward_workspace_bytes for these M,
+ * flags and shard_index) exceeds TPMLP_NOALLOC_SCRATCH_BYTES returns
+ * TPMLP_ERR_WORKSPACE before any HIP call (at D = 1024, F = 4096 every
+ * option fits up to M = 4096 rows).  All calls on one GPU share that GPU's array, which
+ * keeps the last call's contents: calls that may overlap on one GPU (on
+ * different streams, or from different threads) race and must be
+ * serialised by the caller.  Errors: those of tpmlp_forward_ex, and
+ * TPMLP_ERR_HIP if the array's device address cannot be obtained.
+ */
+tpmlp_status tpmlp_forward_noalloc(const void* X, int64_t M, const tpmlp_shards* s, void* Y,
+                                   const tpmlp_opts* opts, void* stream);
+
 /*
  * Bytes of device workspace tpmlp_backward needs for M rows: three M x F
  * intermediates in the weights' dtype (S = X A, H = GeLU(S) and dS), plus

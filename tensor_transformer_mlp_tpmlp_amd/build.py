@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["tpmlp_api.cpp", "attention_api.cpp", "elementwise.hip", "gemm_generic.hip", "gemm_bf16.hip",
-           "attention.hip"]
+           "attention.hip", "noalloc.hip"]
 
 # -packed-fp32-ops: never emit packed fp32 VALU instructions (v_pk_*_f32).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

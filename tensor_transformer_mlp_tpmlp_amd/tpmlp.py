@@ -59,6 +59,7 @@ SIGNATURES = {
     "tpmlp_forward": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp]),
     "tpmlp_opts_init": (None, [ctypes.POINTER(Opts)]),
     "tpmlp_forward_ex": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, ctypes.POINTER(Opts), _c_vp]),
+    "tpmlp_forward_noalloc": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, ctypes.POINTER(Opts), _c_vp]),
     "tpmlp_backward_workspace_bytes": (_c_sz, [_c_vp, _c_i64]),
     "tpmlp_backward": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "tpmlp_attn_pack_bytes": (_c_sz, [_c_i64, _c_int, _c_int, _c_int, _c_int]),
