@@ -140,10 +140,8 @@ enum {
  * intermediate H = GeLU(X A_i) for every shard (M x F, or M x F/n for a
  * single shard, in the weights' dtype) plus, with TPMLP_OPT_LAYERNORM, two
  * fp32 per-row statistics, plus, with TPMLP_OPT_LAYERNORM_AFTER, the
- * M x D fp32 sum that is normalised, plus fp32 partial sums (S x M x D) when the
- * second GEMM has too few output tiles to fill the GPU and splits its
- * K loop S ways.  The size depends on the device's compute-unit count.
- * Returns 0 for invalid arguments.
+ * M x D fp32 sum that is normalised.  Nothing else: the shard sum never
+ * leaves the second GEMM's accumulators.  Returns 0 for invalid arguments.
  * `single_shard` != 0 sizes it for a forward restricted to one shard.
  */
 size_t tpmlp_forward_workspace_bytes(const tpmlp_shards* s, int64_t M, int flags, int single_shard);

@@ -64,6 +64,7 @@ GemmArgs proj_shape(int64_t M, int64_t N, int64_t K) {
     g.C = fake; g.ldc = N; g.c_dtype = kBF16;
     g.epi = kEpiStore;
     g.ab_dtype = kBF16;
+    g.allow_split = true;
     return g;
 }
 

@@ -9,17 +9,18 @@
 //     launch (shard i is the N range iF/n..(i+1)F/n-1), GeLU fused in the
 //     epilogue, H stored in bf16;
 //   * row-parallel GEMM2 (bullet 2 and the sum of bullet 3): Aop = H,
-//     Bop = packed B^T; the K loop runs over every shard's rows, so all
-//     partials Y_i are summed in the same fp32 accumulator and never leave
-//     the chip.
+//     Bop = packed B^T; each output tile's K loop runs over every shard's
+//     rows, so all partials Y_i are summed in the same fp32 accumulator and
+//     only the sum is written.  The forward never splits this K loop: when
+//     its output has few tiles, narrower tiles fill the GPU instead.
 //
-// Tiling: one 256x256 output tile per workgroup of 4 waves (2x2, one wave per
-// SIMD), each wave owning a 128x128 sub-tile: 8x8 MFMA blocks of 16x16, 256
-// fp32 accumulators per lane held in AGPRs.  Shapes too small to fill the GPU
-// with 256x256 tiles use 128x128 tiles (4x4 blocks per wave, 80 KiB of LDS,
-// two workgroups per CU) with the same pipeline.  K advances 64 per step;
-// each operand's 64-wide slice of a step is a "unit" (32 KiB at 256x256),
-// and a ring of five unit slots fills the 160 KiB of LDS.
+// Tiling: one BM x BN output tile per workgroup of 4 waves (2x2, one wave
+// per SIMD), each wave owning a (BM/2) x (BN/2) sub-tile of 16x16 MFMA
+// blocks with its fp32 accumulators in AGPRs (256 per lane at 256x256).
+// The tile shapes are 256x256, 128x128, 128x64 and 64x64; the host picks
+// the one that fills the GPU best (see choose_cfg).  K advances 64 per step;
+// each operand's 64-wide slice of a step is a "unit" (BM or BN rows of 128
+// bytes), and a ring of NU unit slots holds the units in flight.
 //
 // The 16x16x32 MFMA is used rather than 32x32x16: with random operands it
 // sustains a higher clock under the chip's power limit for the same FLOP.
@@ -32,14 +33,22 @@
 // LDS base + 16 L, so the XOR swizzle of the LDS layout is applied on the
 // global side by choosing which 16-byte chunk each lane fetches.
 //
-// Pipeline: step t computes two 32-deep sub-steps from units A_t and B_t.
-// Sub-step 0 reads the fragments of sub-step 1 and issues the loads of
-// A_{t+2}; a barrier then publishes A_{t+1}, B_{t+1} and frees A_t, B_t;
-// sub-step 1 reads the next step's first fragments and issues B_{t+2} into
-// A_t's slot.  Each load covers whole 128-byte lines (8 rows x 128 bytes),
-// the unit the L1 fetches from L2 in, so a step costs the CU's load path the
-// fewest requests; loads and reads are spread evenly between the MFMAs.  A
-// load of B has more than one sub-step, a load of A more than two, to land.
+// Pipeline: unit u of the K loop is A_t for u = 2t and B_t for u = 2t + 1;
+// it lives in ring slot u mod NU.  Step t computes two 32-deep sub-steps
+// from A_t and B_t.  Sub-step 0 reads the fragments of sub-step 1 and issues
+// unit 2t + NU - 1 into the slot of B_{t-1}; a barrier then publishes
+// A_{t+1}, B_{t+1} and frees A_t, B_t; sub-step 1 reads the next step's
+// first fragments and issues unit 2t + NU into the slot of A_t.  A unit is
+// therefore issued (NU - 3) / 2 steps or more before the barrier that
+// publishes it.  Each load covers whole 128-byte lines (8 rows x 128
+// bytes), the unit the L1 fetches from L2 in, and loads and reads are
+// spread evenly between the MFMAs.
+//
+// Ragged shapes: M and N need not be whole tiles.  Each lane's load rows
+// are clamped to the last row of the operand, so an edge tile reads only
+// rows that exist (its extra rows repeat the last one and their results
+// are discarded), and the epilogue stores only rows below M and columns
+// below N.  K must be a whole number of 64-wide steps.
 //
 // LayerNorm prologue (FFN half of the Post-LN block, "LLM Lab Notes 06",
 // section 2, marker 5) is applied algebraically in GEMM1's epilogue:
@@ -57,19 +66,37 @@ namespace tpmlp {
 
 namespace {
 
-// WB: the tile is 64*WB square; 4 gives 256x256 (128x128 per wave), 2 gives
-// 128x128 (64x64 per wave), used when 256x256 tiles would leave CUs idle.
-// K advances BK = 64 per step, two 16x16x32 MFMA sub-steps.  The operands
-// of a step live in LDS as two "units", one per operand (M rows of 128
-// bytes), in a ring of NUNIT unit slots.
+// K advances BK = 64 per step, two 16x16x32 MFMA sub-steps.
 constexpr int BK = 64;
-constexpr int NUNIT = 5;
-template <int WB> struct Tile {
-    static constexpr int M = 64 * WB;             // tile rows (= tile columns)
-    static constexpr int UNIT_BYTES = M * BK * 2;  // one operand of one step
-    static constexpr int NB = 2 * WB;             // 16x16 MFMA blocks per wave per side
-    static constexpr int LPU = M / 32;            // direct loads per wave per unit
+constexpr int kLdsBytes = 160 * 1024;
+
+// A tile shape: BM x BN output tile, NU ring slots.  Each wave owns NBM x NBN
+// blocks of 16x16; a unit of Aop is BM rows of 128 bytes (UA), of Bop BN rows
+// (UB); a slot holds either.  A wave issues LPA (LPB) direct loads of 1 KiB
+// per unit of Aop (Bop).
+template <int BM_, int BN_, int NU_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, NU = NU_;
+    static constexpr int NBM = BM / 32, NBN = BN / 32;
+    static constexpr int UA = BM * BK * 2, UB = BN * BK * 2;
+    static constexpr int SLOT = UA > UB ? UA : UB;
+    static constexpr int LPA = BM / 32, LPB = BN / 32;
+    // loads in flight at a steady barrier: units 2t+4 .. 2t+NU-1, starting with an Aop unit
+    static constexpr int VM_STEADY = ((NU - 3) / 2) * LPA + ((NU - 4) / 2) * LPB;
+    // bf16 output staged through LDS after the K loop: each wave's
+    // (BM/2) x (BN/2) block in rows of BN bytes plus 16 bytes of padding
+    static constexpr int OUT_PITCH = BN + 16;
+    static constexpr int OUT_WAVE = (BM / 2) * OUT_PITCH;
+    static_assert(4 * OUT_WAVE <= NU * SLOT, "the staged output must fit in the ring");
+    static_assert(NU >= 5, "the ring needs the four units of two steps plus one in flight");
+    static_assert(NU * SLOT <= kLdsBytes, "the ring must fit in LDS");
+    static_assert(BM % 64 == 0 && BN % 64 == 0, "tile edges of whole 64-row load groups");
 };
+
+using C256 = Cfg<256, 256, 5>;    // one workgroup per CU
+using C128 = Cfg<128, 128, 5>;    // two per CU
+using C128x64 = Cfg<128, 64, 10>; // one per CU, units issued 3 steps ahead
+using C64 = Cfg<64, 64, 10>;      // two per CU, units issued 3 steps ahead
 
 // The GeLU epilogue that also stores the pre-activation (GemmArgs::preact_out
 // set), and the GeLU-derivative epilogue that also stores GeLU of its operand
@@ -124,7 +151,7 @@ __device__ __forceinline__ uint32_t lds_key(uint32_t r) { return ((r & 8) >> 2) 
 // Rows start on the same bank (their length is a multiple of 256 bytes); a
 // transposing fragment read takes 32 bytes from each of 16 rows 8 g + 4 h + i
 // (g = 0..3, i = 0..3), and the key gives the rows of each half-wave eight
-// distinct 32-byte bank groups.
+// distinct 32-byte bank groups.  Needs rows of at least 16 chunks (BM >= 128).
 __device__ __forceinline__ uint32_t kswz(uint32_t r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
 
 
@@ -188,14 +215,32 @@ __device__ __forceinline__ void gelu_tanh_staged(f32x4 (&v)[N]) {
         for (int r = 0; r < 4; ++r) v[j][r] = v[j][r] * z[j][r];
 }
 
-template <int WB, int EPI, bool LN, typename TC, int KM>
+// Per-load byte offsets of one lane into a row-major operand unit of R rows
+// (R/4 rows per wave, LP = R/32 loads of 8 rows each).  In load q lane L
+// fills unit row w R/4 + 8 q + L/8 at physical chunk L % 8, which must hold
+// logical chunk (L % 8) ^ key(row).  The source row is clamped to the last
+// of the operand's `rows` rows (r0 is the tile's first row, where the
+// buffer resource starts).
+template <int R, int LP>
+__device__ __forceinline__ void row_load_offsets(uint32_t (&v)[LP], int w, int lane, int64_t r0, int64_t rows,
+                                                 int64_t ld) {
+#pragma unroll
+    for (int q = 0; q < LP; ++q) {
+        const uint32_t row = (uint32_t)(w * (R / 4) + 8 * q + (lane >> 3));
+        const int64_t src = min(r0 + (int64_t)row, rows - 1) - r0;
+        v[q] = (uint32_t)(src * ld * 2) + ((((uint32_t)lane & 7u) ^ lds_key(row)) << 4);
+    }
+}
+
+template <class C, int EPI, bool LN, typename TC, int KM>
 __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     constexpr bool KA = (KM & 1) != 0, KB = (KM & 2) != 0;  // operand stored K-major
-    constexpr int BM = Tile<WB>::M, BN = Tile<WB>::M;
-    constexpr int NB = Tile<WB>::NB;
-    constexpr int UB = Tile<WB>::UNIT_BYTES;
-    constexpr int LPU = Tile<WB>::LPU;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[NUNIT * UB];
+    constexpr int BM = C::BM, BN = C::BN, NU = C::NU;
+    constexpr int NBM = C::NBM, NBN = C::NBN;
+    constexpr int SLOT = C::SLOT;
+    constexpr int LPA = C::LPA, LPB = C::LPB;
+    static_assert(!KM || (BM >= 128 && BN >= 128), "K-major units need rows of at least 16 chunks");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NU * SLOT];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -210,72 +255,80 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
 
     // Buffer resources over this tile's rows of each operand, from its K range
     // on; a K-major operand's resource starts at row k0, column m0 (n0) and
-    // runs to the end of the operand.
-    const uint32_t a_bytes = KA ? (uint32_t)((p.K - k0) * p.lda * 2 - m0 * 2) : (uint32_t)(BM * p.lda * 2 - k0 * 2);
-    const uint32_t b_bytes = KB ? (uint32_t)((p.K - k0) * p.ldb * 2 - n0 * 2) : (uint32_t)(BN * p.ldb * 2 - k0 * 2);
+    // runs to the end of the operand.  (K-major operands come in whole tiles.)
+    const int64_t rows_a = min((int64_t)BM, (int64_t)p.M - m0), rows_b = min((int64_t)BN, (int64_t)p.N - n0);
+    const uint32_t a_bytes = KA ? (uint32_t)((p.K - k0) * p.lda * 2 - m0 * 2) : (uint32_t)(rows_a * p.lda * 2 - k0 * 2);
+    const uint32_t b_bytes = KB ? (uint32_t)((p.K - k0) * p.ldb * 2 - n0 * 2) : (uint32_t)(rows_b * p.ldb * 2 - k0 * 2);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16*>(KA ? p.A + k0 * p.lda + m0 : p.A + m0 * p.lda + k0), (short)0, (int)a_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16*>(KB ? p.B + k0 * p.ldb + n0 : p.B + n0 * p.ldb + k0), (short)0, (int)b_bytes, 0x00020000);
+    // The same with no records: every load through it is out of range, reads
+    // no memory and writes zeros to LDS.  The ring issues its last units
+    // through these (see the main loop).
+    const __amdgpu_buffer_rsrc_t ra0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(p.A), (short)0, 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(p.B), (short)0, 0, 0x00020000);
 
-    // Wave w fills rows [w BM/4, (w+1) BM/4) of a unit with LPU loads of 8
-    // rows (1 KiB); in load q, lane L fills row w BM/4 + 8 q + L/8 at physical
-    // chunk L % 8, which must hold logical chunk (L % 8) ^ key(row), and
-    // row % 16 = 8 (q & 1) + L/8 since BM/4 is a multiple of 16.
-    const uint32_t lrow = (uint32_t)(w * (BM / 4) + (lane >> 3));
-    const uint32_t cx0 = ((uint32_t)(lane & 7) ^ lds_key((uint32_t)lane >> 3)) << 4;
-    const uint32_t cx1 = ((uint32_t)(lane & 7) ^ lds_key(8u + ((uint32_t)lane >> 3))) << 4;
-    const uint32_t a_v0 = lrow * (uint32_t)(p.lda * 2) + cx0, a_v1 = a_v0 - cx0 + cx1;
-    const uint32_t b_v0 = lrow * (uint32_t)(p.ldb * 2) + cx0, b_v1 = b_v0 - cx0 + cx1;
-    const uint32_t a_qstep = (uint32_t)(8 * p.lda * 2);
-    const uint32_t b_qstep = (uint32_t)(8 * p.ldb * 2);
-    const uint32_t dst_w = (uint32_t)(w * (BM / 4) * 128);
+    // row-major operands: per-load lane offsets (rows clamped to the operand)
+    uint32_t va[KA ? 1 : LPA], vb[KB ? 1 : LPB];
+    if constexpr (!KA) row_load_offsets<BM, LPA>(va, w, lane, m0, p.M, p.lda);
+    if constexpr (!KB) row_load_offsets<BN, LPB>(vb, w, lane, n0, p.N, p.ldb);
+    const uint32_t dst_a = (uint32_t)(w * (BM / 4) * 128), dst_b = (uint32_t)(w * (BN / 4) * 128);
 
     // slot s of the ring
-    auto slot = [&](int s) { return ring + s * UB; };
+    auto slot = [&](int s) { return ring + s * SLOT; };
 
     // the same resources as SGPR dwords for the inline-assembly loads
-    u32x4 ra4 = {}, rb4 = {};
+    u32x4 ra4 = {}, rb4 = {}, ra40 = {}, rb40 = {};
     if constexpr (KM != 0) {
         ra4 = buffer_rsrc_sgpr(KA ? p.A + k0 * p.lda + m0 : p.A + m0 * p.lda + k0, a_bytes);
         rb4 = buffer_rsrc_sgpr(KB ? p.B + k0 * p.ldb + n0 : p.B + n0 * p.ldb + k0, b_bytes);
+        ra40 = buffer_rsrc_sgpr(p.A, 0u);
+        rb40 = buffer_rsrc_sgpr(p.B, 0u);
     }
 
-    // K-major operand units: 64 rows (k) of RB = 2 BM bytes (the tile's columns),
-    // 16-byte chunk c of row r at physical chunk c ^ kswz(r).  Wave w fills
-    // rows 16 w .. 16 w + 15 with LPU loads of 1 KiB; in load q lane L lands at
-    // row 16 w + q RPL + L / CPR, physical chunk L % CPR.
-    constexpr int RB = BM * 2, CPR = RB / 16, RPL = 64 / CPR;
-    uint32_t kv_a[KA ? LPU : 1], kv_b[KB ? LPU : 1];
+    // K-major operand units: 64 rows (k) of 2 BM (2 BN) bytes (the tile's
+    // columns), 16-byte chunk c of row r at physical chunk c ^ kswz(r).  Wave
+    // w fills rows 16 w .. 16 w + 15 with LP loads of 1 KiB; in load q lane L
+    // lands at row 16 w + q RPL + L / CPR, physical chunk L % CPR.
+    constexpr int RBA = BM * 2, CPRA = RBA / 16, RPLA = 64 / CPRA;
+    constexpr int RBB = BN * 2, CPRB = RBB / 16, RPLB = 64 / CPRB;
+    uint32_t kv_a[KA ? LPA : 1], kv_b[KB ? LPB : 1];
+    if constexpr (KA) {
 #pragma unroll
-    for (int q = 0; q < LPU; ++q) {
-        const uint32_t r = (uint32_t)(16 * w + q * RPL + lane / CPR);
-        const uint32_t c = ((uint32_t)(lane % CPR) ^ kswz(r)) << 4;
-        if constexpr (KA) kv_a[q] = r * (uint32_t)(p.lda * 2) + c;
-        if constexpr (KB) kv_b[q] = r * (uint32_t)(p.ldb * 2) + c;
-    }
-
-    // load q of the unit of operand `op` (0 = Aop, 1 = Bop) at k0 into slot st
-    // (with a K-major operand every load goes through dma16_asm, since the
-    // transposing reads would wait for any direct load the compiler sees)
-    auto load_one = [&](uint8_t* st, int op, int k0, int q) {
-        const uint32_t kb = (uint32_t)k0 * 2u;
-        uint8_t* dst = st + dst_w + q * 1024;
-        const __amdgpu_buffer_rsrc_t r = op ? rb : ra;
-        uint32_t voff, soff;
-        if (op) {
-            if constexpr (KB) { voff = kv_b[q]; soff = (uint32_t)k0 * (uint32_t)(p.ldb * 2); }
-            else { voff = (q & 1) ? b_v1 : b_v0; soff = kb + q * b_qstep; }
-        } else {
-            if constexpr (KA) { voff = kv_a[q]; soff = (uint32_t)k0 * (uint32_t)(p.lda * 2); }
-            else { voff = (q & 1) ? a_v1 : a_v0; soff = kb + q * a_qstep; }
+        for (int q = 0; q < LPA; ++q) {
+            const uint32_t r = (uint32_t)(16 * w + q * RPLA + lane / CPRA);
+            kv_a[q] = r * (uint32_t)(p.lda * 2) + (((uint32_t)(lane % CPRA) ^ kswz(r)) << 4);
         }
-        if constexpr (KM != 0) dma16_asm(dst, op ? rb4 : ra4, voff, soff);
-        else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
-    };
-    auto load_unit = [&](uint8_t* st, int op, int k0) {
+    }
+    if constexpr (KB) {
 #pragma unroll
-        for (int q = 0; q < LPU; ++q) load_one(st, op, k0, q);
+        for (int q = 0; q < LPB; ++q) {
+            const uint32_t r = (uint32_t)(16 * w + q * RPLB + lane / CPRB);
+            kv_b[q] = r * (uint32_t)(p.ldb * 2) + (((uint32_t)(lane % CPRB) ^ kswz(r)) << 4);
+        }
+    }
+
+    // load q of the unit of operand `op` (0 = Aop, 1 = Bop) of K step kstep
+    // into slot st, through the empty resource when !real (with a K-major
+    // operand every load goes through dma16_asm, since the transposing reads
+    // would wait for any direct load the compiler sees)
+    auto load_one = [&](uint8_t* st, int op, int kstep, int q, bool real) {
+        const uint32_t kb = (uint32_t)kstep * (uint32_t)(BK * 2);
+        uint32_t voff, soff;
+        uint8_t* dst;
+        if (op) {
+            dst = st + dst_b + q * 1024;
+            if constexpr (KB) { voff = kv_b[q]; soff = (uint32_t)(kstep * BK) * (uint32_t)(p.ldb * 2); }
+            else { voff = vb[q]; soff = kb; }
+        } else {
+            dst = st + dst_a + q * 1024;
+            if constexpr (KA) { voff = kv_a[q]; soff = (uint32_t)(kstep * BK) * (uint32_t)(p.lda * 2); }
+            else { voff = va[q]; soff = kb; }
+        }
+        if constexpr (KM != 0) dma16_asm(dst, op ? (real ? rb4 : rb40) : (real ? ra4 : ra40), voff, soff);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? (real ? rb : rb0) : (real ? ra : ra0), (lds_void*)dst, 16,
+                                                      voff, soff, 0, 0);
     };
 
     // MFMA operand reads: a 16x16x32 fragment is 16 rows x 32 k; in sub-step
@@ -283,8 +336,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // 4 kk + (l >> 4).  The same lane -> k assignment for both operands makes
     // each MFMA a plain 32-long dot product per output.
     const uint32_t kr = lds_key((uint32_t)lane & 15);
-    const uint32_t rd_a = (uint32_t)((wm * 16 * NB + (lane & 15)) * 128);
-    const uint32_t rd_b = (uint32_t)((wn * 16 * NB + (lane & 15)) * 128);
+    const uint32_t rd_a = (uint32_t)((wm * 16 * NBM + (lane & 15)) * 128);
+    const uint32_t rd_b = (uint32_t)((wn * 16 * NBN + (lane & 15)) * 128);
     const uint32_t ch0 = (((uint32_t)(lane >> 4)) ^ kr) << 4;
     const uint32_t ch1 = (((uint32_t)(4 + (lane >> 4))) ^ kr) << 4;
 
@@ -296,23 +349,30 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // same order as a row-major fragment.  kf_*[f] is fragment f's byte offset
     // in the unit at sub-step 0, h = 0; sub-step kk and half h add
     // (32 kk + 4 h) RB.
-    uint32_t kf_a[KA ? NB : 1], kf_b[KB ? NB : 1];
+    uint32_t kf_a[KA ? NBM : 1], kf_b[KB ? NBN : 1];
     {
         const uint32_t li = (uint32_t)lane & 15, g = (uint32_t)lane >> 4;
         const uint32_t row = 8 * g + (li >> 2);
         const uint32_t sw = kswz(row);
+        if constexpr (KA) {
 #pragma unroll
-        for (int f = 0; f < NB; ++f) {
-            const uint32_t col_a = (uint32_t)(wm * 16 * NB + 16 * f) + 4 * (li & 3);
-            const uint32_t col_b = (uint32_t)(wn * 16 * NB + 16 * f) + 4 * (li & 3);
-            if constexpr (KA) kf_a[f] = row * RB + ((((col_a >> 3) ^ sw)) << 4) + ((col_a & 7) << 1);
-            if constexpr (KB) kf_b[f] = row * RB + ((((col_b >> 3) ^ sw)) << 4) + ((col_b & 7) << 1);
+            for (int f = 0; f < NBM; ++f) {
+                const uint32_t col = (uint32_t)(wm * 16 * NBM + 16 * f) + 4 * (li & 3);
+                kf_a[f] = row * RBA + ((((col >> 3) ^ sw)) << 4) + ((col & 7) << 1);
+            }
+        }
+        if constexpr (KB) {
+#pragma unroll
+            for (int f = 0; f < NBN; ++f) {
+                const uint32_t col = (uint32_t)(wn * 16 * NBN + 16 * f) + 4 * (li & 3);
+                kf_b[f] = row * RBB + ((((col >> 3) ^ sw)) << 4) + ((col & 7) << 1);
+            }
         }
     }
-    auto read_frag = [&](const uint8_t* unit, uint32_t off, int kk) -> bf16x8 {
-        const uint8_t* q = unit + off + kk * 32 * RB;
+    auto read_frag = [&](const uint8_t* unit, uint32_t off, int kk, int rb) -> bf16x8 {
+        const uint8_t* q = unit + off + kk * 32 * rb;
         const v4s lo = lds_read_tr16(q);
-        const v4s hi = lds_read_tr16(q + 4 * RB);
+        const v4s hi = lds_read_tr16(q + 4 * rb);
         bf16x8 r;
         __builtin_memcpy(&r, &lo, 8);
         __builtin_memcpy(reinterpret_cast<uint8_t*>(&r) + 8, &hi, 8);
@@ -330,195 +390,249 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // longer sees are covered explicitly: the AGPR writes of the zero
     // initialisation before the first MFMA reads them, and the last MFMA's
     // results before the epilogue reads them.
-    f32x4 acc[NB][NB];
+    f32x4 acc[NBM][NBN];
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
+    for (int i = 0; i < NBM; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
+        for (int j = 0; j < NBN; ++j) {
             acc[i][j] = f32x4{};
             asm volatile("" : "+a"(acc[i][j]));
         }
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 
-    bf16x8 fa0[NB], fb0[NB], fa1[NB], fb1[NB];
-    const int nk = kc / BK;
-    __builtin_assume(nk >= 3);
+    bf16x8 fa0[NBM], fb0[NBN], fa1[NBM], fb1[NBN];
+    const int nk = kc / BK;   // >= 1
 
     // Per sub-step: NM MFMAs; the NR fragment reads of the next sub-step go
-    // one after every RS-th MFMA from the first, the LPU direct loads of one
-    // unit one after every LS-th.
-    constexpr int NM = NB * NB, NR = 2 * NB, RS = NM / NR / 2 > 0 ? NM / NR / 2 : 1;
-    constexpr int LS = NM / LPU;
-    static_assert(NM % LPU == 0 && (NR - 1) * RS < NM, "sub-step layout");
+    // one after every RS-th MFMA from the first, the direct loads of one unit
+    // one after every NM/LP-th.
+    constexpr int NM = NBM * NBN, NR = NBM + NBN, RS = NM / NR / 2 > 0 ? NM / NR / 2 : 1;
+    static_assert(NM % LPA == 0 && NM % LPB == 0, "sub-step layout");
 
-    // One sub-step: MFMAs on (fc, gc); read the next fragments at chunk
-    // offset ch from units ua (Aop) and ub (Bop) into (fn, gn); when
-    // `load_op` >= 0, issue the unit of operand load_op at k_load into slot
-    // `dst`.
     auto frag_a = [&](const uint8_t* ua, uint32_t ch, int kk, int f) -> bf16x8 {
-        if constexpr (KA) return read_frag(ua, kf_a[f], kk);
+        if constexpr (KA) return read_frag(ua, kf_a[f], kk, RBA);
         else return *reinterpret_cast<const bf16x8*>(ua + rd_a + ch + f * 2048);
     };
     auto frag_b = [&](const uint8_t* ub, uint32_t ch, int kk, int f) -> bf16x8 {
-        if constexpr (KB) return read_frag(ub, kf_b[f], kk);
+        if constexpr (KB) return read_frag(ub, kf_b[f], kk, RBB);
         else return *reinterpret_cast<const bf16x8*>(ub + rd_b + ch + f * 2048);
     };
-    auto sub_step = [&](const bf16x8 (&fc)[NB], const bf16x8 (&gc)[NB], const uint8_t* ua, const uint8_t* ub,
-                        uint32_t ch, int kk, bf16x8 (&fn)[NB], bf16x8 (&gn)[NB], bool do_read, uint8_t* dst,
-                        int load_op, int k_load) {
+    // One sub-step: MFMAs on (fc, gc); read the next fragments at chunk
+    // offset ch, sub-step kk, from units ua (Aop) and ub (Bop) into (fn, gn)
+    // when do_read; with OP = 0 (1) issue the Aop (Bop) unit of K step ks
+    // into slot dst (through the empty resource when !real), with OP = -1
+    // nothing.
+    auto sub_step = [&](const bf16x8 (&fc)[NBM], const bf16x8 (&gc)[NBN], const uint8_t* ua, const uint8_t* ub,
+                        uint32_t ch, int kk, bf16x8 (&fn)[NBM], bf16x8 (&gn)[NBN], bool do_read, auto op_c,
+                        uint8_t* dst, int ks, bool real) {
+        constexpr int OP = decltype(op_c)::value;
+        constexpr int LP = OP == 1 ? LPB : LPA;
+        constexpr int LS = NM / LP;
 #pragma unroll
         for (int idx = 0; idx < NM; ++idx) {
-            const int i = idx / NB, j = idx % NB;
+            const int i = idx / NBN, j = idx % NBN;
             asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(gc[j]), "v"(fc[i]));
             if (do_read && idx % RS == 0 && idx / RS < NR) {
-                // fragment reads in consumption order: Aop 0, Bop 0..NB-1, Aop 1..NB-1
+                // fragment reads in consumption order: Aop 0, Bop 0..NBN-1, Aop 1..NBM-1
                 const int r = idx / RS;
                 if (r == 0) fn[0] = frag_a(ua, ch, kk, 0);
-                else if (r <= NB) gn[r - 1] = frag_b(ub, ch, kk, r - 1);
-                else fn[r - NB] = frag_a(ua, ch, kk, r - NB);
+                else if (r <= NBN) gn[r - 1] = frag_b(ub, ch, kk, r - 1);
+                else fn[r - NBN] = frag_a(ua, ch, kk, r - NBN);
             }
-            if (load_op >= 0 && idx % LS == 0) load_one(dst, load_op, k_load, idx / LS);
+            if constexpr (OP >= 0)
+                if (idx % LS == 0) load_one(dst, OP, ks, idx / LS, real);
         }
     };
 
-    // Step t reads units A_t, B_t (ring slots 2t, 2t+1 mod NUNIT).  Sub-step
-    // 0 issues A_{t+2} into the slot of B_{t-1}; the barrier between the
-    // sub-steps publishes A_{t+1}, B_{t+1} and frees A_t, B_t; sub-step 1
-    // issues B_{t+2} into the slot of A_t.  A load of B has more than one
-    // sub-step, a load of A more than two, to land before the barrier that
-    // publishes it.
-    auto next = [](int s, int d) { s += d; return s >= NUNIT ? s - NUNIT : s; };
+    auto next = [](int s, int d) { s += d; return s >= NU ? s - NU : s; };
     auto barrier_wait = [&](auto vm_left) {
         __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(decltype(vm_left)::value));
         __builtin_amdgcn_s_barrier();
     };
 
-    // prologue: units A_0, B_0, A_1, B_1, A_2 into slots 0..4; wait for step 0
-    load_unit(slot(0), 0, 0);
-    load_unit(slot(1), 1, 0);
-    load_unit(slot(2), 0, BK);
-    load_unit(slot(3), 1, BK);
-    load_unit(slot(4), 0, 2 * BK);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LPU));
+    // Units past the last one (u >= 2 nk) are issued like the others but
+    // through the empty resources: they read nothing and fill slots nobody
+    // reads again with zeros.  So every step but the last has the same code
+    // and the same count of loads in flight at its barrier (one loop, whose
+    // register assignment stays fixed: two loops let the allocator move an
+    // accumulator through VGPRs between the inline-assembly MFMAs, which the
+    // compiler cannot pad for).
+    // prologue: units 0 .. NU-2; wait for A_0 and B_0
+#pragma unroll
+    for (int u = 0; u < NU - 1; ++u) {
+        uint8_t* st = slot(u);
+        const bool real = u < 2 * nk;
+        if (u & 1) {
+#pragma unroll
+            for (int q = 0; q < LPB; ++q) load_one(st, 1, u >> 1, q, real);
+        } else {
+#pragma unroll
+            for (int q = 0; q < LPA; ++q) load_one(st, 0, u >> 1, q, real);
+        }
+    }
+    constexpr int VM_PRO = ((NU - 2) / 2) * LPA + ((NU - 3) / 2) * LPB;  // units 2 .. NU-2
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_PRO));
     __builtin_amdgcn_s_barrier();
     {
         fa0[0] = frag_a(slot(0), ch0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) fb0[j] = frag_b(slot(1), ch0, 0, j);
+        for (int j = 0; j < NBN; ++j) fb0[j] = frag_b(slot(1), ch0, 0, j);
 #pragma unroll
-        for (int i = 1; i < NB; ++i) fa0[i] = frag_a(slot(0), ch0, 0, i);
+        for (int i = 1; i < NBM; ++i) fa0[i] = frag_a(slot(0), ch0, 0, i);
     }
 
-    // step 0: A_2 is already in flight
-    sub_step(fa0, fb0, slot(0), slot(1), ch1, 1, fa1, fb1, true, nullptr, -1, 0);
-    barrier_wait(ic<LPU>{});
-    sub_step(fa1, fb1, slot(2), slot(3), ch0, 0, fa0, fb0, true, slot(0), 1, 2 * BK);
-
-    // steps 1 .. nk-3
-    int sa = 2;  // slot of A_t
-    for (int kt = 1; kt + 2 < nk; ++kt) {
-        const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3), sa2 = next(sa, 4);
-        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, 1, fa1, fb1, true, slot(sa2), 0, (kt + 2) * BK);
-        barrier_wait(ic<LPU>{});
-        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, 0, fa0, fb0, true, slot(sa), 1, (kt + 2) * BK);
+    // Sub-step 0 of step t issues unit 2t + NU - 1 (into the slot of B_{t-1},
+    // which is slot(sa) - 1), sub-step 1 unit 2t + NU (into the slot of A_t);
+    // their operands are fixed by the parity of NU.  Every barrier leaves the
+    // units 2t+4 .. 2t+NU-1 in flight.
+    constexpr int OP0 = (NU - 1) & 1, OP1 = NU & 1;
+    int sa = 0;  // slot of A_t
+    for (int tt = 0; tt < nk - 1; ++tt) {
+        const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3), sp = next(sa, NU - 1);
+        const int u0 = 2 * tt + NU - 1;
+        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, 1, fa1, fb1, true, ic<OP0>{}, slot(sp), u0 >> 1, u0 < 2 * nk);
+        barrier_wait(ic<C::VM_STEADY>{});
+        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, 0, fa0, fb0, true, ic<OP1>{}, slot(sa), (u0 + 1) >> 1,
+                 u0 + 1 < 2 * nk);
         sa = sa1;
     }
-    // step nk-2: nothing left to load
-    {
-        const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3);
-        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, 1, fa1, fb1, true, nullptr, -1, 0);
-        barrier_wait(ic<0>{});
-        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, 0, fa0, fb0, true, nullptr, -1, 0);
-        sa = sa1;
-    }
-    // step nk-1
-    sub_step(fa0, fb0, slot(sa), slot(next(sa, 1)), ch1, 1, fa1, fb1, true, nullptr, -1, 0);
+    // the last step: nothing left to load or to read ahead; the empty loads
+    // still in flight (the last units of the ring) finish before the epilogue
+    sub_step(fa0, fb0, slot(sa), slot(next(sa, 1)), ch1, 1, fa1, fb1, true, ic<-1>{}, nullptr, 0, false);
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
-    sub_step(fa1, fb1, slot(sa), slot(sa), ch0, 0, fa0, fb0, false, nullptr, -1, 0);
+    sub_step(fa1, fb1, slot(sa), slot(sa), ch0, 0, fa0, fb0, false, ic<-1>{}, nullptr, 0, false);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // a bf16 output is staged in the ring's LDS: every wave must be done
+    // reading its last units first
+    constexpr bool kStage = std::is_same<TC, bf16>::value;
+    if constexpr (kStage) __builtin_amdgcn_s_barrier();
     // results of the last MFMAs are read by the epilogue
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     // Epilogue: lane l writes row m = ... + (l & 15) of block i, columns
     // n .. n+3 with n = ... + 4 (l >> 4) of block j.  A whole row block is
-    // transformed before it is stored, which gives the scheduler NB * 4
+    // transformed before it is stored, which gives the scheduler NBN * 4
     // independent GeLU chains to interleave.
-    TC* __restrict__ C = static_cast<TC*>(p.C) + kz * p.c_split_stride;
-    const int64_t n_base = n0 + wn * 16 * NB + 4 * (lane >> 4);
-    const int64_t m_base = m0 + wm * 16 * NB + (lane & 15);
+    //
+    // Every epilogue access goes through a buffer resource that starts at
+    // this tile's first row and column and ends after its last row below M,
+    // and a column at or past N gets the offset kOut, past every resource:
+    // the hardware's range check then drops the stores of rows and columns
+    // outside the matrix and returns zero for such loads, with no branch and
+    // no clamping (edge tiles of ragged shapes; interior tiles pay one add
+    // per access).
+    constexpr uint32_t kOut = 0x80000000u;
+    const int64_t rows_t = min((int64_t)BM, (int64_t)p.M - m0);
+    const int64_t cols_t = (int64_t)p.N - n0;
+    const uint32_t lr = (uint32_t)(wm * 16 * NBM + (lane & 15));       // lane's row in the tile, block 0
+    const uint32_t lc = (uint32_t)(wn * 16 * NBN + 4 * (lane >> 4));   // lane's column in the tile, block 0
+    uint32_t cb2[NBN], cbc[NBN];  // column byte offsets for 2-byte elements and for C's, or kOut
+#pragma unroll
+    for (int j = 0; j < NBN; ++j) {
+        const bool in = (int64_t)(lc + 16 * j) < cols_t;
+        cb2[j] = in ? (lc + 16 * j) * 2u : kOut;
+        cbc[j] = in ? (lc + 16 * j) * (uint32_t)sizeof(TC) : kOut;
+    }
+    auto rsrc = [&](const void* base, int64_t ld, int es) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void*>(base), (short)0, (int)(rows_t * ld * es), 0x00020000);
+    };
+    TC* __restrict__ Cp = static_cast<TC*>(p.C) + kz * p.c_split_stride;
+    const auto rc = rsrc(Cp + m0 * p.ldc + n0, p.ldc, (int)sizeof(TC));
+    constexpr bool kGrad = EPI == kEpiGeluGrad || EPI == kEpiGeluGradSave;
+    constexpr bool kHasAux = kGrad || EPI == kEpiStore;
     // The epilogue's operand (the pre-activation, or the residual) is read
     // for the whole wave tile before the first row block is transformed, so
     // its memory latency is paid once rather than once per row block.
-    constexpr bool kGrad = EPI == kEpiGeluGrad || EPI == kEpiGeluGradSave;
-    constexpr bool kHasAux = kGrad || EPI == kEpiStore;
-    bf16x4 ex[kHasAux ? NB : 1][kHasAux ? NB : 1];
-    if constexpr (kGrad) {
+    bf16x4 ex[kHasAux ? NBM : 1][kHasAux ? NBN : 1];
+    if constexpr (kHasAux) {
+        const bf16* src = kGrad ? p.aux : p.R;
+        const int64_t ld = kGrad ? p.ldaux : p.ldr;
+        if (kGrad || p.R) {
+            const auto rx = rsrc(src + m0 * ld + n0, ld, 2);
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
+            for (int i = 0; i < NBM; ++i)
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                ex[i][j] = *reinterpret_cast<const bf16x4*>(p.aux + (m_base + i * 16) * p.ldaux + n_base + j * 16);
-    } else if constexpr (EPI == kEpiStore) {
-        if (p.R) {
-#pragma unroll
-            for (int i = 0; i < NB; ++i)
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    ex[i][j] = *reinterpret_cast<const bf16x4*>(p.R + (m_base + i * 16) * p.ldr + n_base + j * 16);
+                for (int j = 0; j < NBN; ++j)
+                    ex[i][j] = __builtin_bit_cast(
+                        bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                    rx, (lr + 16 * i) * (uint32_t)(ld * 2) + cb2[j], 0, 0));
         }
     }
+    // one row block of bf16 stores (or C's dtype) at offsets row + cb[j], non-temporal when asked
+    auto store_row = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t row_off, const uint32_t (&cb)[NBN],
+                         const f32x4 (&v)[NBN], bool as_f32) {
+        if (p.nt_store) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int64_t m = m_base + i * 16;
-        f32x4 v[NB];
+            for (int j = 0; j < NBN; ++j) {
+                if (as_f32) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[j]), r, row_off + cb[j], 0, 2);
+                else {
+                    bf16x4 o;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) v[j] = acc[i][j];
+                    for (int q = 0; q < 4; ++q) o[q] = static_cast<bf16>(v[j][q]);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), r, row_off + cb[j], 0, 2);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NBN; ++j) {
+                if (as_f32) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[j]), r, row_off + cb[j], 0, 0);
+                else {
+                    bf16x4 o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) o[q] = static_cast<bf16>(v[j][q]);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), r, row_off + cb[j], 0, 0);
+                }
+            }
+        }
+    };
+    __amdgpu_buffer_rsrc_t r_mean = rc, r_rstd = rc, r_csum = rc;
+    if constexpr (LN) {
+        r_mean = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.mean + m0), (short)0, (int)(rows_t * 4), 0x00020000);
+        r_rstd = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.rstd + m0), (short)0, (int)(rows_t * 4), 0x00020000);
+        r_csum = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.csum + n0), (short)0, (int)(cols_t * 4), 0x00020000);
+    }
+#pragma unroll
+    for (int i = 0; i < NBM; ++i) {
+        const uint32_t row = lr + 16 * i;
+        f32x4 v[NBN];
+#pragma unroll
+        for (int j = 0; j < NBN; ++j) v[j] = acc[i][j];
         if constexpr (LN) {
-            const float rs = p.rstd[m];
-            const float rm = rs * p.mean[m];
+            const float rs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_rstd, row * 4u, 0, 0));
+            const float rm = rs * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_mean, row * 4u, 0, 0));
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const f32x4 cs = *reinterpret_cast<const f32x4*>(p.csum + n_base + j * 16);
+            for (int j = 0; j < NBN; ++j) {
+                const f32x4 cs = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(r_csum, (lc + 16 * j) * 4u, 0, 0));
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[j][r] = __builtin_fmaf(rs, v[j][r], -rm * cs[r]);
             }
         }
         if constexpr (EPI == kEpiGelu || EPI == kEpiGeluSave) {
-            if constexpr (EPI == kEpiGeluSave) {
-                // the pre-activation, kept for a backward pass
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    bf16x4 o;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(v[j][r]);
-                    bf16x4* dst = reinterpret_cast<bf16x4*>(p.preact + m * p.ldc + n_base + j * 16);
-                    if (p.nt_store) __builtin_nontemporal_store(o, dst);
-                    else *dst = o;
-                }
-            }
+            if constexpr (EPI == kEpiGeluSave)  // the pre-activation, kept for a backward pass
+                store_row(rsrc(p.preact + m0 * p.ldc + n0, p.ldc, 2), row * (uint32_t)(p.ldc * 2), cb2, v, false);
             gelu_tanh_staged(v);
         } else if constexpr (kGrad) {
             if constexpr (EPI == kEpiGeluGradSave) {
                 // GeLU of the pre-activation (the forward's H), for the
                 // gradient of the second weight
+                f32x4 h[NBN];
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    bf16x4 o;
+                for (int j = 0; j < NBN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(gelu_tanh(static_cast<float>(ex[i][j][r])));
-                    bf16x4* dst = reinterpret_cast<bf16x4*>(p.gelu_out + m * p.ldc + n_base + j * 16);
-                    if (p.nt_store) __builtin_nontemporal_store(o, dst);
-                    else *dst = o;
-                }
+                    for (int r = 0; r < 4; ++r) h[j][r] = gelu_tanh(static_cast<float>(ex[i][j][r]));
+                store_row(rsrc(p.gelu_out + m0 * p.ldc + n0, p.ldc, 2), row * (uint32_t)(p.ldc * 2), cb2, h, false);
             }
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
+            for (int j = 0; j < NBN; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[j][r] *= gelu_tanh_grad(static_cast<float>(ex[i][j][r]));
         } else {
             if (p.R) {
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
+                for (int j = 0; j < NBN; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) v[j][r] += static_cast<float>(ex[i][j][r]);
             }
@@ -527,28 +641,44 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
         // it would not fit the caches anyway, and keeping it out of them
         // keeps the operands resident in the Infinity Cache.  A small one
         // stays cached for its reader.
+        if constexpr (kStage) {
+            // lane l: row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. +3 of the wave's block
+            uint8_t* st = ring + w * C::OUT_WAVE + (16 * i + (lane & 15)) * C::OUT_PITCH + 8 * (lane >> 4);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            TC* row = C + m * p.ldc + n_base + j * 16;
-            if constexpr (std::is_same<TC, float>::value) {
-                f32x4* dst = reinterpret_cast<f32x4*>(row);
-                if (p.nt_store) __builtin_nontemporal_store(v[j], dst);
-                else *dst = v[j];
-            } else {
+            for (int j = 0; j < NBN; ++j) {
                 bf16x4 o;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(v[j][r]);
-                bf16x4* dst = reinterpret_cast<bf16x4*>(row);
-                if (p.nt_store) __builtin_nontemporal_store(o, dst);
-                else *dst = o;
+                for (int q = 0; q < 4; ++q) o[q] = static_cast<bf16>(v[j][q]);
+                *reinterpret_cast<bf16x4*>(st + 32 * j) = o;
             }
+        } else {
+            store_row(rc, row * (uint32_t)(p.ldc * sizeof(TC)), cbc, v, true);
+        }
+    }
+    if constexpr (kStage) {
+        // The wave's block back from LDS in whole rows: lane l reads 16 bytes
+        // (8 columns) of row 4 q + l / CPR at chunk l % CPR, so one store
+        // instruction writes whole 128-byte lines of RPI rows.  Rows at or
+        // past M fall outside the resource; N is a multiple of 8, so a chunk
+        // lies wholly below N or wholly at or past it (kOut).
+        constexpr int CPR = BN / 16, RPI = 64 / CPR, NQ = (BM / 2) / RPI;
+        const uint32_t c = (uint32_t)(lane % CPR), rq = (uint32_t)(lane / CPR);
+        const uint32_t colo = (uint32_t)(wn * (BN / 2)) + 8 * c;
+        const uint32_t cb = (int64_t)colo < cols_t ? colo * 2u : kOut;
+        const uint8_t* src = ring + w * C::OUT_WAVE + rq * C::OUT_PITCH + 16 * c;
+        const uint32_t r0 = (uint32_t)(wm * (BM / 2)) + rq;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const u32x4 d = *reinterpret_cast<const u32x4*>(src + q * RPI * C::OUT_PITCH);
+            const uint32_t off = (r0 + q * RPI) * (uint32_t)(p.ldc * 2) + cb;
+            if (p.nt_store) __builtin_amdgcn_raw_buffer_store_b128(d, rc, off, 0, 2);
+            else __builtin_amdgcn_raw_buffer_store_b128(d, rc, off, 0, 0);
         }
     }
 }
 
-template <int WB, int EPI, typename TC, int KM = 0>
+template <class C, int EPI, typename TC, int KM = 0>
 hipError_t launch_typed(const GemmArgs& g, int splits, hipStream_t stream) {
-    constexpr int BM = Tile<WB>::M, BN = Tile<WB>::M;
     FastParams p;
     p.A = static_cast<const bf16*>(g.A); p.lda = g.lda;
     p.B = static_cast<const bf16*>(g.B); p.ldb = g.ldb;
@@ -559,19 +689,25 @@ hipError_t launch_typed(const GemmArgs& g, int splits, hipStream_t stream) {
     p.aux = static_cast<const bf16*>(g.aux); p.ldaux = g.ldaux;
     p.preact = static_cast<bf16*>(g.preact_out);
     p.gelu_out = static_cast<bf16*>(g.gelu_out);
-    p.tiles_m = (int)(g.M / BM);
-    p.tiles_n = (int)(g.N / BN);
+    p.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
+    p.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
     p.group = 4;
     p.nt_store = g.M * g.N * (int64_t)sizeof(TC) > ((int64_t)128 << 20);
     p.splits = splits;
     p.c_split_stride = splits > 1 ? g.M * g.N : 0;
     const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n * splits);
-    if constexpr (KM != 0)
-        gemm_bf16_mfma<WB, EPI, false, TC, KM><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-    else if (g.ln_mean)
-        gemm_bf16_mfma<WB, EPI, true, TC, 0><<<dim3(blocks), dim3(256), 0, stream>>>(p);
-    else
-        gemm_bf16_mfma<WB, EPI, false, TC, 0><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+    // the LayerNorm epilogue exists for the forward's epilogues only (the
+    // GeLU-derivative ones never see a LayerNorm)
+    constexpr bool kLnVariant = KM == 0 && EPI != kEpiGeluGrad && EPI != kEpiGeluGradSave;
+    if constexpr (kLnVariant) {
+        if (g.ln_mean) {
+            gemm_bf16_mfma<C, EPI, true, TC, 0><<<dim3(blocks), dim3(256), 0, stream>>>(p);
+            return hipGetLastError();
+        }
+    } else {
+        if (g.ln_mean) return hipErrorInvalidValue;
+    }
+    gemm_bf16_mfma<C, EPI, false, TC, KM><<<dim3(blocks), dim3(256), 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -592,31 +728,61 @@ int device_cu_count() {
 }
 static int device_cus() { return device_cu_count(); }
 
-// Whether the MFMA kernel can take a shape with tiles of 64*wb rows: bf16
-// operands, M and N whole tiles, K a whole number (at least three) of
-// 64-wide steps, 16-byte aligned rows, one operand tile's byte offsets below 2^31
-// (buffer offsets), and, with the LayerNorm epilogue, the column sums of Bop.
+// Tile configurations (0: not for the MFMA kernel).
+enum TileCfg { kCfgNone = 0, kCfg256 = 1, kCfg128 = 2, kCfg128x64 = 3, kCfg64 = 4 };
+struct CfgInfo {
+    int bm, bn;
+    int per_cu;     // workgroups a CU holds at once (LDS)
+    double step;    // time of one 64-deep K step of one tile at that occupancy, relative to 256x256
+};
+static CfgInfo cfg_info(int c) {
+    // 128x128: a round of two tiles per CU does half the work of a 256x256
+    // round in 0.515 of its time (measured at K = 1024); the narrower tiles
+    // are costed at the same MFMA-rate loss per halving.
+    switch (c) {
+        case kCfg256: return {256, 256, 1, 1.0};
+        case kCfg128: return {128, 128, 2, 0.515};
+        case kCfg128x64: return {128, 64, 1, 0.265};
+        case kCfg64: return {64, 64, 2, 0.27};
+        default: return {0, 0, 0, 0.0};
+    }
+}
+
+// Whether the MFMA kernel can take a shape with a given tile: bf16 operands,
+// K a whole number of 64-wide steps, 16-byte aligned rows, one operand tile's
+// byte offsets below 2^31 (buffer offsets), and, with the LayerNorm
+// epilogue, the column sums of Bop.  M and N may be ragged (row-major
+// operands only); N must be a multiple of 4 (the epilogue's quads).
 // K-major operands: Bop alone (store or GeLU-derivative epilogue) or both
-// (store epilogue), without LayerNorm or the pre-activation stash.  The
-// GeLU output of the GeLU-derivative epilogue goes with that epilogue only.
-static bool fits_tile(const GemmArgs& g, int wb) {
-    const int64_t tm = 64 * wb;
+// (store epilogue), without LayerNorm or the pre-activation stash, on whole
+// tiles of at least 128.  The GeLU output of the GeLU-derivative epilogue
+// goes with that epilogue only.
+static bool fits_cfg(const GemmArgs& g, int cfg) {
+    const CfgInfo ci = cfg_info(cfg);
+    if (!ci.bm) return false;
     if (g.ab_dtype != kBF16) return false;
     if (g.M <= 0 || g.N <= 0 || g.K <= 0) return false;
-    if (g.M % tm || g.N % tm || g.K % BK || g.K < 3 * BK) return false;
+    if (g.K % BK || g.N % 4 || (g.c_dtype == kBF16 && g.N % 8)) return false;
+    const bool km = g.a_kmajor || g.b_kmajor;
+    if (km && (ci.bm < 128 || ci.bn < 128 || g.M % ci.bm || g.N % ci.bn)) return false;
     if (g.lda % 8 || g.ldb % 8 || !aligned16(g.A) || !aligned16(g.B)) return false;
     // buffer offsets: a tile's rows of a row-major operand, or all K rows of a K-major one
-    if ((g.a_kmajor ? g.K : tm) * g.lda * 2 >= ((int64_t)1 << 31)) return false;
-    if ((g.b_kmajor ? g.K : tm) * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
+    if ((g.a_kmajor ? g.K : ci.bm) * g.lda * 2 >= ((int64_t)1 << 31)) return false;
+    if ((g.b_kmajor ? g.K : ci.bn) * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
     if (g.a_kmajor && (!g.b_kmajor || g.epi != kEpiStore)) return false;
     if (g.b_kmajor && ((g.epi != kEpiStore && g.epi != kEpiGeluGrad) || g.ln_mean || g.preact_out)) return false;
-    if ((g.M / tm) * (g.N / tm) >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) ||
-        g.N >= ((int64_t)1 << 31) || g.K >= ((int64_t)1 << 31))
+    const int64_t tiles = ((g.M + ci.bm - 1) / ci.bm) * ((g.N + ci.bn - 1) / ci.bn);
+    if (tiles * 8 >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) || g.N >= ((int64_t)1 << 31) ||
+        g.K >= ((int64_t)1 << 31))
         return false;
     if (g.ln_mean && !g.ln_csum) return false;
     // the epilogue moves four consecutive columns per lane: 16-byte (fp32)
-    // or 8-byte (bf16) stores and residual loads, 16-byte column-sum loads
+    // or 8-byte (bf16) stores and residual loads, 16-byte column-sum loads,
+    // all through buffer resources of one tile's rows (offsets below 2^31)
     const int64_t c_es = g.c_dtype == kF32 ? 4 : 2;
+    if (ci.bm * g.ldc * c_es >= ((int64_t)1 << 31) || (g.R && ci.bm * g.ldr * 2 >= ((int64_t)1 << 31)) ||
+        (g.aux && ci.bm * g.ldaux * 2 >= ((int64_t)1 << 31)) || g.N * 4 >= ((int64_t)1 << 31))
+        return false;
     if (g.ldc % 4 || (reinterpret_cast<uintptr_t>(g.C) & (4 * c_es - 1))) return false;
     if (g.R && (g.ldr % 4 || (reinterpret_cast<uintptr_t>(g.R) & 7))) return false;
     if (g.ln_mean && !aligned16(g.ln_csum)) return false;
@@ -628,40 +794,48 @@ static bool fits_tile(const GemmArgs& g, int wb) {
     return true;
 }
 
-// Tile size: 256x256 (wb = 4, one workgroup per CU) or 128x128 (wb = 2, two
-// per CU); 0 = not for the MFMA kernel.  With t 256x256 tiles on C CUs, the
-// 256x256 plan takes ceil(t / C) rounds, a partial round lasting as long as
-// a full one.  A round of 128x128 tiles does half the work of a 256x256
-// round in 0.515 of its time (measured at K = 1024 on MI355X) and, its tiles
-// being finer, a partial round costs about its share: 0.515 * 4 t / (2 C).
-// The cheaper plan wins; 256x256 on a tie (its L2 reuse is better).
-static int choose_wb(const GemmArgs& g) {
-    const bool f4 = fits_tile(g, 4), f2 = fits_tile(g, 2);
-    if (f4 && f2) {
-        const double cus = (double)device_cus();
-        const double t4 = (double)(g.M / 256) * (double)(g.N / 256);
-        const double rounds4 = std::ceil(t4 / cus);
-        const double rounds2 = 0.515 * 4.0 * t4 / (2.0 * cus);
-        return rounds2 < rounds4 ? 2 : 4;
-    }
-    if (f2) return 2;
-    if (f4) return 4;
-    return 0;
+// Modelled time of a GEMM on tile configuration cfg: the tiles run in
+// rounds of (CUs x workgroups per CU); a full round takes the configuration's
+// step time per K step, and the last, partial round its share (a round of
+// fine tiles is balanced by the hardware's dispatch, a partial round of
+// 256x256 tiles costs as much as a full one).
+static double cfg_cost(const GemmArgs& g, int cfg) {
+    const CfgInfo ci = cfg_info(cfg);
+    const double slots = (double)device_cus() * ci.per_cu;
+    const double tiles = (double)((g.M + ci.bm - 1) / ci.bm) * (double)((g.N + ci.bn - 1) / ci.bn);
+    const double rounds = cfg == kCfg256 ? std::ceil(tiles / slots) : std::max(1.0, tiles / slots);
+    return rounds * ci.step * (double)(g.K / BK);
 }
 
-GemmPath choose_gemm_path(const GemmArgs& g) { return choose_wb(g) ? kPathFastBf16 : kPathGeneric; }
+static int choose_cfg(const GemmArgs& g) {
+    int best = kCfgNone;
+    double best_cost = 0.0;
+    for (int c : {kCfg256, kCfg128, kCfg128x64, kCfg64}) {
+        if (!fits_cfg(g, c)) continue;
+        const double cost = cfg_cost(g, c);
+        if (best == kCfgNone || cost < best_cost) {  // ties keep the larger tile (better L2 reuse)
+            best = c;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
 
-// Split-K plan: a GEMM with a plain store epilogue and no LayerNorm whose
-// output tiles fill at most a quarter of the workgroup slots (two per CU at
-// 128x128, one at 256x256) runs its K loop as S equal ranges, S the largest
-// power of two (at most 8) that keeps tiles x S within the slots and each
-// range a whole number (at least three) of 64-wide steps.  Each range
-// writes fp32 partial sums; split_reduce_kernel adds them in range order.
-static int split_count(const GemmArgs& g, int wb) {
-    if (g.epi != kEpiStore || g.ln_mean) return 1;
-    const int64_t tm = 64 * wb;
-    const int64_t tiles = (g.M / tm) * (g.N / tm);
-    const int64_t slots = (int64_t)device_cus() * (wb == 2 ? 2 : 1);
+GemmPath choose_gemm_path(const GemmArgs& g) { return choose_cfg(g) ? kPathFastBf16 : kPathGeneric; }
+
+// Split-K plan: only a GEMM that allows it (GemmArgs::allow_split: the
+// backward's weight gradients and the attention projections, never the
+// forward's shard sum), with a plain store epilogue and no LayerNorm, whose
+// output tiles fill at most a quarter of the workgroup slots, runs its K loop
+// as S equal ranges, S the largest power of two (at most 8) that keeps
+// tiles x S within the slots and each range a whole number (at least three)
+// of 64-wide steps.  Each range writes fp32 partial sums; split_reduce_kernel
+// adds them in range order.
+static int split_count(const GemmArgs& g, int cfg) {
+    if (!g.allow_split || g.epi != kEpiStore || g.ln_mean) return 1;
+    const CfgInfo ci = cfg_info(cfg);
+    const int64_t tiles = ((g.M + ci.bm - 1) / ci.bm) * ((g.N + ci.bn - 1) / ci.bn);
+    const int64_t slots = (int64_t)device_cus() * ci.per_cu;
     if (tiles * 4 > slots) return 1;
     int s = 1;
     while (s < 8 && tiles * s * 2 <= slots && g.K % (2 * s * BK) == 0 && g.K / (2 * s) >= 3 * BK) s *= 2;
@@ -669,9 +843,9 @@ static int split_count(const GemmArgs& g, int wb) {
 }
 
 size_t gemm_split_bytes(const GemmArgs& g) {
-    const int wb = choose_wb(g);
-    if (!wb) return 0;
-    const int s = split_count(g, wb);
+    const int cfg = choose_cfg(g);
+    if (!cfg) return 0;
+    const int s = split_count(g, cfg);
     return s > 1 ? (size_t)s * (size_t)g.M * (size_t)g.N * sizeof(float) : 0;
 }
 
@@ -679,7 +853,7 @@ namespace {
 
 // C[m][n] = sum over r = 0..S-1, in that order, of part[r][m][n] (+ R[m][n]),
 // rounded to C's dtype: the epilogue of a split GEMM.  Four columns per
-// thread (N is a multiple of 128).
+// thread (N is a multiple of 4).
 template <typename TC>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int S, int64_t M,
                                                           int64_t N, const bf16* __restrict__ R, int64_t ldr,
@@ -710,9 +884,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 }  // namespace
 
 // Store epilogue, with the split-K plan when it applies.
-template <int WB, int KM>
-static hipError_t launch_store(const GemmArgs& g, hipStream_t stream) {
-    const int s = split_count(g, WB);
+template <class C, int KM>
+static hipError_t launch_store(const GemmArgs& g, int cfg, hipStream_t stream) {
+    const int s = split_count(g, cfg);
     if (s > 1) {
         // K ranges write fp32 partials, then one pass sums them
         GemmArgs gp = g;
@@ -720,7 +894,7 @@ static hipError_t launch_store(const GemmArgs& g, hipStream_t stream) {
         gp.ldc = g.N;
         gp.c_dtype = kF32;
         gp.R = nullptr;
-        hipError_t e = launch_typed<WB, kEpiStore, float, KM>(gp, s, stream);
+        hipError_t e = launch_typed<C, kEpiStore, float, KM>(gp, s, stream);
         if (e != hipSuccess) return e;
         const int64_t quads = g.M * g.N / 4;
         const unsigned blocks = (unsigned)std::min<int64_t>((quads + 255) / 256, 8 * (int64_t)device_cus());
@@ -734,35 +908,46 @@ static hipError_t launch_store(const GemmArgs& g, hipStream_t stream) {
                                                                            static_cast<bf16*>(g.C), g.ldc);
         return hipGetLastError();
     }
-    return g.c_dtype == kF32 ? launch_typed<WB, kEpiStore, float, KM>(g, 1, stream)
-                             : launch_typed<WB, kEpiStore, bf16, KM>(g, 1, stream);
+    return g.c_dtype == kF32 ? launch_typed<C, kEpiStore, float, KM>(g, 1, stream)
+                             : launch_typed<C, kEpiStore, bf16, KM>(g, 1, stream);
 }
 
-template <int WB>
-static hipError_t launch_wb(const GemmArgs& g, hipStream_t stream) {
-    // K-major operands (fits_tile admits Bop alone or both, with the store or
-    // GeLU-derivative epilogue and no LayerNorm)
-    if (g.a_kmajor && g.b_kmajor) return launch_store<WB, 3>(g, stream);
-    if (g.b_kmajor) {
-        if (g.epi == kEpiGeluGrad)
-            return g.gelu_out ? launch_typed<WB, kEpiGeluGradSave, bf16, 2>(g, 1, stream)
-                              : launch_typed<WB, kEpiGeluGrad, bf16, 2>(g, 1, stream);
-        return launch_store<WB, 2>(g, stream);
-    }
-    if (g.epi == kEpiGelu)
-        return g.preact_out ? launch_typed<WB, kEpiGeluSave, bf16>(g, 1, stream)
-                            : launch_typed<WB, kEpiGelu, bf16>(g, 1, stream);
+// K-major operands (fits_cfg admits Bop alone or both, with the store or
+// GeLU-derivative epilogue and no LayerNorm), on the two square tiles.
+template <class C>
+static hipError_t launch_kmajor(const GemmArgs& g, int cfg, hipStream_t stream) {
+    if (g.a_kmajor) return launch_store<C, 3>(g, cfg, stream);
     if (g.epi == kEpiGeluGrad)
-        return g.gelu_out ? launch_typed<WB, kEpiGeluGradSave, bf16>(g, 1, stream)
-                          : launch_typed<WB, kEpiGeluGrad, bf16>(g, 1, stream);
-    return launch_store<WB, 0>(g, stream);
+        return g.gelu_out ? launch_typed<C, kEpiGeluGradSave, bf16, 2>(g, 1, stream)
+                          : launch_typed<C, kEpiGeluGrad, bf16, 2>(g, 1, stream);
+    return launch_store<C, 2>(g, cfg, stream);
+}
+
+template <class C>
+static hipError_t launch_rowmajor(const GemmArgs& g, int cfg, hipStream_t stream) {
+    if (g.epi == kEpiGelu)
+        return g.preact_out ? launch_typed<C, kEpiGeluSave, bf16>(g, 1, stream)
+                            : launch_typed<C, kEpiGelu, bf16>(g, 1, stream);
+    if (g.epi == kEpiGeluGrad)
+        return g.gelu_out ? launch_typed<C, kEpiGeluGradSave, bf16>(g, 1, stream)
+                          : launch_typed<C, kEpiGeluGrad, bf16>(g, 1, stream);
+    return launch_store<C, 0>(g, cfg, stream);
 }
 
 hipError_t launch_gemm_bf16_fast(const GemmArgs& g, hipStream_t stream) {
+    const int cfg = choose_cfg(g);
+    if (!cfg) return hipErrorInvalidValue;
     if (gemm_split_bytes(g) > 0 && (!g.split_ws || g.split_ws_bytes < gemm_split_bytes(g) ||
                                     (reinterpret_cast<uintptr_t>(g.split_ws) & 15)))
         return hipErrorInvalidValue;
-    return choose_wb(g) == 2 ? launch_wb<2>(g, stream) : launch_wb<4>(g, stream);
+    if (g.a_kmajor || g.b_kmajor)
+        return cfg == kCfg256 ? launch_kmajor<C256>(g, cfg, stream) : launch_kmajor<C128>(g, cfg, stream);
+    switch (cfg) {
+        case kCfg256: return launch_rowmajor<C256>(g, cfg, stream);
+        case kCfg128: return launch_rowmajor<C128>(g, cfg, stream);
+        case kCfg128x64: return launch_rowmajor<C128x64>(g, cfg, stream);
+        default: return launch_rowmajor<C64>(g, cfg, stream);
+    }
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {

@@ -39,9 +39,12 @@ struct GemmArgs {
     int64_t ldaux = 0;
     void* preact_out = nullptr;  // kEpiGelu: also store the pre-activation here (M x N, ldc, C's dtype)
     void* gelu_out = nullptr;    // kEpiGeluGrad: also store GeLU_tanh(aux) here (M x N, ldc, C's dtype)
-    // Split-K scratch (fp32 partial sums); gemm_split_bytes(g) bytes.  Only
-    // a GEMM that would leave most of the GPU idle (few output tiles, long
-    // K, a plain store epilogue) is split; the others ignore it.
+    // Split-K: a GEMM that allows it and would leave most of the GPU idle
+    // (few output tiles, long K, a plain store epilogue) runs its K loop as
+    // several ranges whose fp32 partial sums go to split_ws
+    // (gemm_split_bytes(g) bytes) and are then added.  The forward's second
+    // GEMM (the shard sum) never allows it: its sum stays in one accumulator.
+    bool allow_split = false;
     void* split_ws = nullptr;
     size_t split_ws_bytes = 0;
     // K-major operands: with a_kmajor, Aop[m][k] = A[k * lda + m] (A stored

@@ -45,28 +45,15 @@ tpmlp_status check_shard_args(int64_t D, int64_t F, int n, int dtype) {
     return TPMLP_OK;
 }
 
-// GEMM2's shape as the forward launches it, with stand-in (aligned) operand
-// pointers: what the workspace size depends on.
-GemmArgs gemm2_shape(const tpmlp_shards* s, int64_t M, int64_t nh) {
-    GemmArgs g;
-    char* const fake = reinterpret_cast<char*>((uintptr_t)256);
-    g.A = fake; g.lda = nh;
-    g.B = fake; g.ldb = s->F;
-    g.M = M; g.N = s->D; g.K = nh;
-    g.C = fake; g.ldc = s->D; g.c_dtype = s->dtype;
-    g.epi = kEpiStore;
-    g.ab_dtype = s->dtype;
-    return g;
-}
-
 // Workspace layout for a forward over M rows with N_h intermediate columns:
 //   [H: M x N_h, weights' dtype][mean: M fp32][rstd: M fp32]
-//   [Z = residual + Y: M x D fp32, normalised last]
-//   [GEMM2 split-K partials: S x M x D fp32, when GEMM2 is split],
+//   [Z = residual + Y: M x D fp32, normalised last],
 // each segment 256-byte aligned; the statistics exist only with the
-// LayerNorm before, Z only with the LayerNorm after.
+// LayerNorm before, Z only with the LayerNorm after.  GEMM2 never splits
+// its K loop (the shard sum stays in one accumulator), so it needs no
+// scratch of its own.
 struct WsLayout {
-    size_t h_off, mean_off, rstd_off, z_off, split_off, split_bytes, total;
+    size_t h_off, mean_off, rstd_off, z_off, total;
 };
 
 WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard) {
@@ -83,9 +70,6 @@ WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard
     }
     L.z_off = off;
     if (flags & TPMLP_OPT_LAYERNORM_AFTER) off += round_up((size_t)M * (size_t)s->D * 4);
-    L.split_off = off;
-    L.split_bytes = M > 0 ? gemm_split_bytes(gemm2_shape(s, M, nh)) : 0;
-    off += round_up(L.split_bytes);
     L.total = off;
     return L;
 }
@@ -107,6 +91,7 @@ struct BwdPtrs {
 GemmArgs bwd_args(const tpmlp_shards* s, int64_t M, int which, const BwdPtrs& q) {
     const int64_t D = s->D, F = s->F;
     GemmArgs g;
+    g.allow_split = true;
     g.ab_dtype = s->dtype;
     g.c_dtype = s->dtype;
     g.epi = kEpiStore;
@@ -364,7 +349,9 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
 
     // GEMM2, row-parallel with the shard sum in the accumulator:
     // Y = H[:, 0:nh] . B^T[:, n_lo:n_lo+nh]^T (+ residual), or, with the
-    // LayerNorm after, Z = residual + Y kept in fp32 for the Norm
+    // LayerNorm after, Z = residual + Y kept in fp32 for the Norm.  Its K loop
+    // is never split (allow_split stays false): every shard's partial goes
+    // into the same fp32 accumulator and only the sum is stored.
     float* Z = ln_after ? reinterpret_cast<float*>(wsb + L.z_off) : nullptr;
     if (e == hipSuccess) {
         GemmArgs g2;
@@ -379,8 +366,6 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
         g2.R = o.residual; g2.ldr = D;
         g2.epi = kEpiStore;
         g2.ab_dtype = s->dtype;
-        g2.split_ws = wsb + L.split_off;
-        g2.split_ws_bytes = L.split_bytes;
         e = launch_gemm(g2, hs);
     }
     // out = LayerNorm(Z), one rounding to Y's dtype
