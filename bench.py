@@ -148,8 +148,9 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload:
 
     def kind(name):
         if "gemm_bf16_mfma" in name:
-            epi = name.split("gemm_bf16_mfma")[1]
-            return "gemm1" if epi.startswith("ILi4ELi0") or epi.startswith("ILi2ELi0") else "gemm2"
+            # gemm_bf16_mfma<Cfg<BM, BN, NU>, EPI, ...>: EPI 0 is GEMM1's GeLU epilogue
+            epi = name.split("Cfg")[1].split("EEE", 1)[1]
+            return "gemm1" if epi.startswith("Li0E") else "gemm2"
         if "copy" in name or "elementwise" in name:
             return "copy"
         return None

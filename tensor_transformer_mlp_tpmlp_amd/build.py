@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -63,11 +64,60 @@ def _compile(src: str) -> str:
     return obj
 
 
+# The throughput GEMM issues its MFMAs as inline assembly with the
+# accumulators tied to AGPRs, so the compiler neither tracks their latency
+# nor pads its own instructions against them.  Any accumulator copy the
+# register allocator inserts between the first MFMA and the padding after
+# the last one could read a stale value, and any spill would sit in the K
+# loop.  Both depend on register-allocation choices, so every build checks
+# the generated assembly of every instantiation of that kernel.
+ASM_CHECKED = "gemm_bf16.hip"
+_GEMM_KERNEL = re.compile(r"^(_ZN5tpmlp\S*gemm_bf16_mfma\S*):", re.M)
+
+
+def check_gemm_asm(asm: str) -> list:
+    """Problems in the assembly of the MFMA GEMM kernels (empty if none)."""
+    problems = []
+    for m in _GEMM_KERNEL.finditer(asm):
+        name = m.group(1)
+        end = asm.index(".Lfunc_end", m.end())
+        body = asm[m.end():end].split("\n")
+        meta = asm[end:end + 4000]
+        scratch = re.search(r"; ScratchSize: (\d+)", meta)
+        if scratch and int(scratch.group(1)) != 0:
+            problems.append(f"{name}: {scratch.group(1)} bytes of scratch (spills)")
+        mfma = [k for k, l in enumerate(body) if "v_mfma" in l]
+        pad = [k for k, l in enumerate(body) if l.strip() == "s_nop 7"]
+        if not mfma or len(pad) < 3:
+            problems.append(f"{name}: no MFMA or no padding found")
+            continue
+        for k in range(mfma[0], pad[-3]):
+            if re.search(r"v_accvgpr_(read|write|mov)", body[k]):
+                problems.append(f"{name}: accumulator copy inside the MFMA region: {body[k].strip()}")
+                break
+    return problems
+
+
+def _asm_check() -> None:
+    asm_path = os.path.join(BUILD_DIR, ASM_CHECKED + ".s")
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "--cuda-device-only", "-S", "-x", "hip",
+           os.path.join(CSRC, ASM_CHECKED), "-o", asm_path]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {ASM_CHECKED}:\n{res.stderr}")
+    with open(asm_path) as f:
+        problems = check_gemm_asm(f.read())
+    if problems:
+        raise RuntimeError("the MFMA GEMM's register allocation is unsafe:\n" + "\n".join(problems))
+
+
 def build(verbose: bool = True) -> str:
     """Compile all sources and link libtpmlp.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        check = ex.submit(_asm_check)
         objs = list(ex.map(_compile, SOURCES))
+        check.result()
     tmp = LIB_PATH + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -598,7 +598,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
         const uint32_t row = lr + 16 * i;
         f32x4 v[NBN];
 #pragma unroll
-        for (int j = 0; j < NBN; ++j) v[j] = acc[i][j];
+        for (int j = 0; j < NBN; ++j) {
+            // the empty asm orders this read after the s_nop padding that
+            // follows the last MFMAs (volatile asm keeps its order; a plain
+            // register copy could be hoisted above the padding)
+            asm volatile("" : "+a"(acc[i][j]));
+            v[j] = acc[i][j];
+        }
         if constexpr (LN) {
             const float rs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_rstd, row * 4u, 0, 0));
             const float rm = rs * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_mean, row * 4u, 0, 0));

@@ -148,18 +148,19 @@ def test_ring_short_k(M, D, F, n):
     assert_close(to_f64(Y), oracle_forward(inp.X, inp.A, inp.B, n), "bf16", f"M={M} D={D} F={F} n={n}")
 
 
-def test_split_k_short_ranges_residual_fp32():
-    """GEMM2 with 64 output tiles of 128x128 splits its K loop 4 ways, each
-    range 3 steps long (K = F = 768); the partial sums, the residual and the
-    fp32 cast meet in the reduction pass."""
+def test_narrow_tiles_short_k_residual_fp32():
+    """GEMM2 with few output tiles (M = D = 1024) and a short K loop
+    (K = F = 768, 12 steps): it runs on narrow tiles with the whole K loop in
+    one accumulator (the forward never splits the shard sum), with the
+    residual and the fp32 cast in its epilogue."""
     M, D, F, n = 1024, 1024, 768, 2
-    say(f"split-K M={M} D={D} F={F} n={n} residual fp32")
+    say(f"narrow tiles, short K, M={M} D={D} F={F} n={n} residual fp32")
     inp = workloads.random_case(M, D, F, seed=77, dtype="bf16")
     Y, _, _ = _run(inp, n, "bf16", residual=True, out_dtype=torch.float32)
     ref = oracle_forward(inp.X, inp.A, inp.B, n, residual=True)
-    assert_close(to_f64(Y), ref, "bf16", "split-K, residual, fp32 out")
+    assert_close(to_f64(Y), ref, "bf16", "narrow tiles, residual, fp32 out")
     Yn, _, _ = _run(inp, n, "bf16")
-    assert_close(to_f64(Yn), oracle_forward(inp.X, inp.A, inp.B, n), "bf16", "split-K, bf16 out")
+    assert_close(to_f64(Yn), oracle_forward(inp.X, inp.A, inp.B, n), "bf16", "narrow tiles, bf16 out")
 
 
 @pytest.mark.parametrize("M,D,F,n", [(512, 256, 1024, 4), (300, 96, 200, 2)])
