@@ -739,18 +739,20 @@ enum TileCfg { kCfgNone = 0, kCfg256 = 1, kCfg128 = 2, kCfg128x64 = 3, kCfg64 = 
 struct CfgInfo {
     int bm, bn;
     int per_cu;     // workgroups a CU holds at once (LDS)
-    double step;    // time of one 64-deep K step of one tile at that occupancy, relative to 256x256
+    double step1;   // time of one 64-deep K step of a tile alone on its CU, relative to 256x256
+    double step2;   // time of one K step of a round with per_cu tiles on each CU (= step1 if per_cu = 1)
 };
+// Measured on MI355X (K steps of the h1024 and Post-LN GEMMs, store and GeLU
+// epilogues): a 128x128 tile alone on a CU takes 0.44 of a 256x256 step, two
+// together 0.515; 128x64 (one per CU, deeper ring) 0.26; 64x64 alone 0.215,
+// two together 0.31.
 static CfgInfo cfg_info(int c) {
-    // 128x128: a round of two tiles per CU does half the work of a 256x256
-    // round in 0.515 of its time (measured at K = 1024); the narrower tiles
-    // are costed at the same MFMA-rate loss per halving.
     switch (c) {
-        case kCfg256: return {256, 256, 1, 1.0};
-        case kCfg128: return {128, 128, 2, 0.515};
-        case kCfg128x64: return {128, 64, 1, 0.265};
-        case kCfg64: return {64, 64, 2, 0.27};
-        default: return {0, 0, 0, 0.0};
+        case kCfg256: return {256, 256, 1, 1.0, 1.0};
+        case kCfg128: return {128, 128, 2, 0.44, 0.515};
+        case kCfg128x64: return {128, 64, 1, 0.26, 0.26};
+        case kCfg64: return {64, 64, 2, 0.215, 0.31};
+        default: return {0, 0, 0, 0.0, 0.0};
     }
 }
 
@@ -800,17 +802,24 @@ static bool fits_cfg(const GemmArgs& g, int cfg) {
     return true;
 }
 
-// Modelled time of a GEMM on tile configuration cfg: the tiles run in
-// rounds of (CUs x workgroups per CU); a full round takes the configuration's
-// step time per K step, and the last, partial round its share (a round of
-// fine tiles is balanced by the hardware's dispatch, a partial round of
-// 256x256 tiles costs as much as a full one).
+// Modelled time of a GEMM on tile configuration cfg: with no more tiles than
+// CUs, one round of tiles alone on their CUs; otherwise rounds of
+// (CUs x workgroups per CU) tiles, the last, partial round costing its share
+// (a round of fine tiles is balanced by the hardware's dispatch, a partial
+// round of 256x256 tiles costs as much as a full one).
 static double cfg_cost(const GemmArgs& g, int cfg) {
     const CfgInfo ci = cfg_info(cfg);
-    const double slots = (double)device_cus() * ci.per_cu;
+    const double cus = (double)device_cus();
     const double tiles = (double)((g.M + ci.bm - 1) / ci.bm) * (double)((g.N + ci.bn - 1) / ci.bn);
-    const double rounds = cfg == kCfg256 ? std::ceil(tiles / slots) : std::max(1.0, tiles / slots);
-    return rounds * ci.step * (double)(g.K / BK);
+    double per_step;
+    if (tiles <= cus) {
+        per_step = ci.step1;
+    } else {
+        const double slots = cus * ci.per_cu;
+        const double rounds = cfg == kCfg256 ? std::ceil(tiles / slots) : std::max(1.0, tiles / slots);
+        per_step = rounds * ci.step2;
+    }
+    return per_step * (double)(g.K / BK);
 }
 
 static int choose_cfg(const GemmArgs& g) {
@@ -842,7 +851,7 @@ static int split_count(const GemmArgs& g, int cfg) {
     const CfgInfo ci = cfg_info(cfg);
     const int64_t tiles = ((g.M + ci.bm - 1) / ci.bm) * ((g.N + ci.bn - 1) / ci.bn);
     const int64_t slots = (int64_t)device_cus() * ci.per_cu;
-    if (tiles * 4 > slots) return 1;
+    if (tiles * 4 > slots) return 1;  // at least a quarter of the slots busy: no split
     int s = 1;
     while (s < 8 && tiles * s * 2 <= slots && g.K % (2 * s * BK) == 0 && g.K / (2 * s) >= 3 * BK) s *= 2;
     return s;
