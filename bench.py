@@ -35,10 +35,16 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 KERNEL_SOURCES = {"gemm1": "tensor_transformer_mlp_tpmlp_amd/csrc/gemm_bf16.hip",
                   "gemm2": "tensor_transformer_mlp_tpmlp_amd/csrc/gemm_bf16.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-# Copy used to calibrate the HBM byte counters: bf16 -> fp32 conversion of
+# Copy used to calibrate the byte counters: bf16 -> fp32 conversion of
 # CALIB_ELEMS elements after the caches were flushed; it reads 2 and writes 4
-# bytes per element.
-CALIB_ELEMS = 256 * 1024 * 1024
+# bytes per element (2 GiB read, 4 GiB written: far beyond the 256 MB
+# Infinity Cache, so every byte crosses from the L2 to memory).
+CALIB_ELEMS = 1 << 30
+# What roofline.traffic measures: FETCH_SIZE and WRITE_SIZE count requests
+# between the L2 and the fabric on one of the L2's memory interfaces; scaled
+# by the calibration copy they estimate all bytes that leave the L2, which
+# the Infinity Cache may serve in part (so they bound HBM traffic from above).
+TRAFFIC_KIND = "bytes between L2 and the fabric (Infinity Cache or HBM), per launch"
 
 
 def log(msg: str) -> None:
@@ -101,8 +107,9 @@ def _sha256(path: str) -> str:
 
 
 def _traffic(workload: str, kernel: str, algorithmic_bytes: float):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    """Bytes between the L2 and the fabric per launch (TRAFFIC_KIND) from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel
+    source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
@@ -111,13 +118,13 @@ def _traffic(workload: str, kernel: str, algorithmic_bytes: float):
     entry = data.get(workload, {}).get(kernel)
     if not entry or entry.get("source_sha256") != _sha256(KERNEL_SOURCES[kernel]):
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry.get("l2_fabric_bytes_per_launch")
 
 
 def copy_calibration() -> None:
     """A plain copy of known size for calibrating FETCH_SIZE / WRITE_SIZE:
     flush the caches with 2 GiB of unrelated writes, then convert
-    CALIB_ELEMS bf16 values (512 MiB read) to fp32 (1 GiB written)."""
+    CALIB_ELEMS bf16 values (2 GiB read) to fp32 (4 GiB written)."""
     import torch
     dev = torch.device("cuda:0")
     src = torch.ones(CALIB_ELEMS, dtype=torch.bfloat16, device=dev)
@@ -132,7 +139,7 @@ def copy_calibration() -> None:
 
 
 def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload: str, out_dir: str,
-                       command: str) -> None:
+                       command: str, sq_dir: str = "") -> None:
     """Turn rocprofv3 CSV output (kernel trace + FETCH_SIZE + WRITE_SIZE runs of
     this bench) into the summaries kept under profiles/."""
     import csv
@@ -173,6 +180,8 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload:
         return per
 
     fetch, write = counter(fetch_dir, "FETCH_SIZE"), counter(write_dir, "WRITE_SIZE")
+    sq = {c: counter(sq_dir, c) for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "TCC_HIT_sum",
+                                          "TCC_MISS_sum")} if sq_dir else {}
 
     def calib(per, expected_kib):
         vals = [v for (k, n, _), v in per.items() if k == "copy" and "bfloat16" in n and "float" in n]
@@ -194,17 +203,43 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload:
     lines += ["", "all kernels (rocprofv3 --stats):", "", "| name | calls | average ns |", "|---|---|---|"]
     for r in stats:
         lines.append(f"| {r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']):.0f} |")
-    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)", "",
+    if sq:
+        import statistics as st
+
+        def mean_of(c, k):
+            v = [x for (kk, _, _), x in sq[c].items() if kk == k]
+            return st.mean(v) if v else None
+        lines += ["", "## MFMA busy, clock and L2 hit rate (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                  "GRBM_GUI_ACTIVE TCC_HIT_sum TCC_MISS_sum)", "",
+                  "GRBM_GUI_ACTIVE is summed over the 8 XCDs, so GRBM_GUI_ACTIVE / 8 is the kernel's length in "
+                  "shader cycles and GRBM_GUI_ACTIVE / 8 / duration its average clock.  MFMA busy = "
+                  "SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs) / (1024 GRBM_GUI_ACTIVE / 8): the "
+                  "fraction of SIMD cycles in which the matrix core was busy.", "",
+                  "| kernel | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | clock GHz (trace duration) | MFMA busy "
+                  "| L2 hit rate |", "|---|---|---|---|---|---|"]
+        for k in ("gemm1", "gemm2"):
+            busy, act = mean_of("SQ_VALU_MFMA_BUSY_CYCLES", k), mean_of("GRBM_GUI_ACTIVE", k)
+            hit, miss = mean_of("TCC_HIT_sum", k), mean_of("TCC_MISS_sum", k)
+            d = durs.get(k)
+            if busy and act and d:
+                cyc = act / 8
+                lines.append(f"| {k} | {busy:.4g} | {act:.4g} | {cyc / (st.mean(d) * 1e3):.2f} | "
+                             f"{busy / (1024 * cyc):.3f} | {hit / (hit + miss):.3f} |")
+    lines += ["", "## Bytes between the L2 and the fabric (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE; "
+              "KiB per dispatch)", "",
+              "FETCH_SIZE and WRITE_SIZE count requests on one of the L2's memory interfaces; they are scaled by "
+              "what they read for the calibration copy.  The bytes leave the L2; the 256 MB Infinity Cache may "
+              "serve part of them, so they bound HBM traffic from above.", "",
               f"calibration copy: {CALIB_ELEMS * 2 >> 20} MiB read / {CALIB_ELEMS * 4 >> 20} MiB written; "
               f"scale factors read {f_read}, write {f_write}", "",
-              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes per launch |", "|---|---|---|---|"]
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes per launch (L2 <-> fabric) |", "|---|---|---|---|"]
     for k in ("gemm1", "gemm2"):
         fv = [v for (kk, _, _), v in fetch.items() if kk == k]
         wv = [v for (kk, _, _), v in write.items() if kk == k]
         if fv and wv and f_read and f_write:
             b = (statistics.mean(fv) * f_read + statistics.mean(wv) * f_write) * 1024
             traffic[k] = {"fetch_kib": statistics.mean(fv), "write_kib": statistics.mean(wv),
-                          "hbm_bytes_per_launch": b, "source_sha256": sha}
+                          "l2_fabric_bytes_per_launch": b, "kind": TRAFFIC_KIND, "source_sha256": sha}
             lines.append(f"| {k} | {statistics.mean(fv):.0f} | {statistics.mean(wv):.0f} | {b:.4g} |")
     os.makedirs(out_dir, exist_ok=True)
     with open(os.path.join(out_dir, f"tpmlp_forward_{workload}.md"), "w") as f:
@@ -525,8 +560,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run the plain copy used to calibrate the HBM byte counters first")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/ summaries from rocprofv3 CSV output of this bench")
+    ap.add_argument("--summarize-profiles", nargs="+", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 CSV output of this bench: TRACE_DIR FETCH_DIR "
+                         "WRITE_DIR [SQ_DIR] (SQ_DIR: SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE TCC_HIT_sum "
+                         "TCC_MISS_sum)")
     ap.add_argument("--profile-command", default="", help="command recorded in the profile summary")
     ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
                     help="time the forward (default, the headline metric) or the backward pass")
@@ -536,8 +573,11 @@ def main() -> int:
 
     if args.summarize_profiles:
         import workloads
-        summarize_profiles(*args.summarize_profiles, args.workload or workloads.HEADLINE,
-                           os.path.join(ROOT, "profiles"), args.profile_command)
+        d = args.summarize_profiles
+        if len(d) not in (3, 4):
+            ap.error("--summarize-profiles takes TRACE_DIR FETCH_DIR WRITE_DIR [SQ_DIR]")
+        summarize_profiles(d[0], d[1], d[2], args.workload or workloads.HEADLINE,
+                           os.path.join(ROOT, "profiles"), args.profile_command, d[3] if len(d) == 4 else "")
         return 0
 
     if args.gpus != 1:
@@ -599,6 +639,8 @@ def main() -> int:
     roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": _traffic(w.name, kernel, 0.0)}
+    if roofline["traffic"] is not None:
+        roofline["traffic_kind"] = TRAFFIC_KIND
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),

@@ -20,8 +20,7 @@ static_assert(TPMLP_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte blocks");
 
 // Nothing in it needs to start at zero: the forward writes every byte of
 // its workspace that it later reads (H, the LayerNorm statistics, the fp32
-// sum of the Norm-after placement, split partial sums).  It keeps the last
-// call's contents.
+// sum of the Norm-after placement).  It keeps the last call's contents.
 static __device__ __align__(256) unsigned char scratch[TPMLP_NOALLOC_SCRATCH_BYTES];
 
 namespace {
