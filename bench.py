@@ -325,8 +325,9 @@ def bench_backward(args, w, inp, X, shards, dtype, dev) -> int:
 
     value = 8·M·D·F / t, the algorithmic FLOP of the four gradient GEMMs.
     As in a training step, the forward (run once, untimed) keeps the
-    pre-activation S = X A, so the backward does not recompute it.  The
-    events bracket the whole pass on the library's stream.
+    pre-activation S = X A and the activation H = GeLU(S), so the backward
+    recomputes neither.  The events bracket the whole pass on the library's
+    stream.
     """
     import numpy as np
     import torch
@@ -342,12 +343,14 @@ def bench_backward(args, w, inp, X, shards, dtype, dev) -> int:
     dY = torch.from_numpy(dYh).to(dev).to(dtype).contiguous()
     outs = (torch.empty_like(X), torch.empty((w.D, w.F), dtype=dtype, device=dev),
             torch.empty((w.F, w.D), dtype=dtype, device=dev))
-    # the forward of a training step keeps the pre-activation for the backward
+    # the forward of a training step keeps the pre-activation and the
+    # activation for the backward
     S = torch.empty((w.M, w.F), dtype=dtype, device=dev)
-    tp.tp_mlp(X, shards, save_preact=S)
+    H = torch.empty((w.M, w.F), dtype=dtype, device=dev)
+    tp.tp_mlp(X, shards, save_preact=S, save_act=H)
 
     def step():
-        tp.tp_mlp_backward(X, dY, shards, out=outs, preact=S)
+        tp.tp_mlp_backward(X, dY, shards, out=outs, preact=S, act=H)
 
     for _ in range(args.warmup):
         step()

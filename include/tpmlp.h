@@ -185,6 +185,11 @@ typedef struct {
     void* save_preact;         /* optional M x F (M x F/n with shard_index), weights' dtype:
                                   receives the pre-activation S = X A (after the LayerNorm
                                   correction) for tpmlp_backward                              */
+    void* save_act;            /* optional M x F (M x F/n with shard_index), weights' dtype:
+                                  receives H = GeLU(S), the activation the second GEMM
+                                  reads, for tpmlp_backward.  GEMM1 writes H here instead
+                                  of into the workspace, so keeping it costs nothing.
+                                  Must not overlap save_preact, X, Y or the workspace.     */
 } tpmlp_opts;
 
 /* Fills *o with the defaults described above. */
@@ -241,8 +246,9 @@ tpmlp_status tpmlp_forward_noalloc(const void* X, int64_t M, const tpmlp_shards*
 
 /*
  * Bytes of device workspace tpmlp_backward needs for M rows: three M x F
- * intermediates in the weights' dtype (S = X A, H = GeLU(S) and dS), plus
- * the split-K scratch of its GEMMs.  No operand is copied or transposed:
+ * intermediates in the weights' dtype (S = X A, H = GeLU(S) and dS; S and
+ * H are not written when the caller passes them), plus the split-K scratch
+ * of its GEMMs.  No operand is copied or transposed:
  * the GEMMs read X, dY, dS, H and the packed weights where they lie.  Returns 0 for
  * invalid arguments.
  */
@@ -264,6 +270,10 @@ size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M);
  *   preact optional M x F pre-activation S = X A saved by a forward without
  *          LayerNorm over all shards (tpmlp_opts.save_preact); NULL recomputes
  *          it (one more GEMM of 2 M D F).
+ *   act    optional M x F activation H = GeLU(S) saved by the same forward
+ *          (tpmlp_opts.save_act): the H whose product with B gave Y.  NULL
+ *          recomputes it from the bf16 S in the epilogue of the dS GEMM (one
+ *          more M x F store and a GeLU per element).
  *   dX     device, M x D, the descriptor's dtype.
  *   dA     device, D x F: dA_i in columns iF/n .. (i+1)F/n - 1 (A's layout).
  *   dB     device, F x D: dB_i in rows iF/n .. (i+1)F/n - 1 (B's layout).
@@ -275,7 +285,8 @@ size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M);
  * returned before any HIP call.
  */
 tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpmlp_shards* s, const void* preact,
-                            void* dX, void* dA, void* dB, void* workspace, size_t workspace_bytes, void* stream);
+                            const void* act, void* dX, void* dA, void* dB, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* ------------------------------------------------------------------------
  * The attention half of the block (head-sharded self-attention).

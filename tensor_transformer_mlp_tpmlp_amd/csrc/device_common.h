@@ -28,22 +28,31 @@ constexpr float kGeluA = 0.044715f;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr float kGeluK0 = (float)(-2.0 * (double)kGeluC * kLog2e);
 constexpr float kGeluK1 = (float)(-2.0 * (double)kGeluC * (double)kGeluA * kLog2e);
-__device__ __forceinline__ float gelu_tanh(float x) {
-    const float z = x * __builtin_fmaf(x * x, kGeluK1, kGeluK0);
-    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
+// s = 1/(1 + exp(-2u)) of x, given x2 = x * x
+__device__ __forceinline__ float gelu_sigmoid(float x, float x2) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * __builtin_fmaf(x2, kGeluK1, kGeluK0)));
 }
+__device__ __forceinline__ float gelu_tanh(float x) { return x * gelu_sigmoid(x, x * x); }
 
 // d/dx GeLU_tanh(x), for the backward pass.  With s = (1 + tanh u)/2 =
 // 1/(1 + exp(-2u)) and 1 - tanh^2 u = 4 s (1 - s), the product and chain
-// rules give s (1 + q (1 - s)), q = 2 sqrt(2/pi) x (1 + 3 * 0.044715 x^2).
-// exp(-2u) overflows to +inf for very negative x; then s = 0 and the result
-// is 0 (without the select, 0 * x^3 could become NaN for huge |x|).
+// rules give s + q s (1 - s), q = 2 sqrt(2/pi) x (1 + 3 * 0.044715 x^2).
+// It is formed as fma(q, t, s) with t = s (1 - s) = fma(-s, s, s) and q =
+// x fma(x^2, q1, q0), sharing x^2 (and the exponential and reciprocal, when
+// GeLU of the same x is also wanted) with gelu_tanh.  At both ends s is
+// exactly 0 or 1, so t = 0 and the result is s (q may overflow there, and
+// q * 0 would be NaN); a NaN x gives a NaN t and result.
+constexpr float kGeluQ0 = (float)(2.0 * (double)kGeluC);
+constexpr float kGeluQ1 = (float)(6.0 * (double)kGeluC * (double)kGeluA);
+// the derivative from x, x2 = x * x and s = gelu_sigmoid(x, x2)
+__device__ __forceinline__ float gelu_grad_from(float x, float x2, float s) {
+    const float q = x * __builtin_fmaf(x2, kGeluQ1, kGeluQ0);
+    const float t = __builtin_fmaf(-s, s, s);
+    const float r = __builtin_fmaf(q, t, s);
+    return t == 0.0f ? s : r;
+}
 __device__ __forceinline__ float gelu_tanh_grad(float x) {
-    const float z = x * __builtin_fmaf(x * x, kGeluK1, kGeluK0);
-    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
-    const float q = (2.0f * kGeluC) * x * __builtin_fmaf((3.0f * kGeluA) * x, x, 1.0f);
-    const float r = s * __builtin_fmaf(q, 1.0f - s, 1.0f);
-    return s == 0.0f ? 0.0f : r;
+    return gelu_grad_from(x, x * x, gelu_sigmoid(x, x * x));
 }
 
 __device__ __forceinline__ float to_f32(float v) { return v; }

@@ -543,22 +543,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     constexpr bool kGrad = EPI == kEpiGeluGrad || EPI == kEpiGeluGradSave;
     constexpr bool kHasAux = kGrad || EPI == kEpiStore;
     // The epilogue's operand (the pre-activation, or the residual) is read
-    // for the whole wave tile before the first row block is transformed, so
-    // its memory latency is paid once rather than once per row block.
+    // EXA row blocks ahead: the first EXA before the first row block is
+    // transformed, then block i + EXA as block i starts, so its memory
+    // latency is paid about once while only EXA + 1 row blocks of it occupy
+    // registers.
+    constexpr int EXA = NBM > 1 ? NBM / 2 : 1;
     bf16x4 ex[kHasAux ? NBM : 1][kHasAux ? NBN : 1];
-    if constexpr (kHasAux) {
-        const bf16* src = kGrad ? p.aux : p.R;
-        const int64_t ld = kGrad ? p.ldaux : p.ldr;
-        if (kGrad || p.R) {
-            const auto rx = rsrc(src + m0 * ld + n0, ld, 2);
+    const bool has_aux = kHasAux && (kGrad || p.R);
+    const bf16* ex_src = kGrad ? p.aux : p.R;
+    const int64_t ex_ld = kGrad ? p.ldaux : p.ldr;
+    const auto rx = rsrc(ex_src + m0 * ex_ld + n0, ex_ld, 2);
+    auto load_ex = [&](int i) {
+        if constexpr (kHasAux) {
 #pragma unroll
-            for (int i = 0; i < NBM; ++i)
-#pragma unroll
-                for (int j = 0; j < NBN; ++j)
-                    ex[i][j] = __builtin_bit_cast(
-                        bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
-                                    rx, (lr + 16 * i) * (uint32_t)(ld * 2) + cb2[j], 0, 0));
+            for (int j = 0; j < NBN; ++j)
+                ex[i][j] = __builtin_bit_cast(
+                    bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rx, (lr + 16 * i) * (uint32_t)(ex_ld * 2) + cb2[j], 0, 0));
         }
+    };
+    if (has_aux) {
+#pragma unroll
+        for (int i = 0; i < EXA; ++i) load_ex(i);
     }
     // one row block of bf16 stores (or C's dtype) at offsets row + cb[j], non-temporal when asked
     auto store_row = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t row_off, const uint32_t (&cb)[NBN],
@@ -595,6 +600,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     }
 #pragma unroll
     for (int i = 0; i < NBM; ++i) {
+        if (has_aux && i + EXA < NBM) load_ex(i + EXA);
         const uint32_t row = lr + 16 * i;
         f32x4 v[NBN];
 #pragma unroll
@@ -623,18 +629,25 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
         } else if constexpr (kGrad) {
             if constexpr (EPI == kEpiGeluGradSave) {
                 // GeLU of the pre-activation (the forward's H), for the
-                // gradient of the second weight
+                // gradient of the second weight, from the same sigmoid as
+                // the derivative
                 f32x4 h[NBN];
 #pragma unroll
                 for (int j = 0; j < NBN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) h[j][r] = gelu_tanh(static_cast<float>(ex[i][j][r]));
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = static_cast<float>(ex[i][j][r]);
+                        const float sg = gelu_sigmoid(x, x * x);
+                        h[j][r] = x * sg;
+                        v[j][r] *= gelu_grad_from(x, x * x, sg);
+                    }
                 store_row(rsrc(p.gelu_out + m0 * p.ldc + n0, p.ldc, 2), row * (uint32_t)(p.ldc * 2), cb2, h, false);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NBN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[j][r] *= gelu_tanh_grad(static_cast<float>(ex[i][j][r]));
             }
-#pragma unroll
-            for (int j = 0; j < NBN; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v[j][r] *= gelu_tanh_grad(static_cast<float>(ex[i][j][r]));
         } else {
             if (p.R) {
 #pragma unroll
@@ -779,6 +792,9 @@ static bool fits_cfg(const GemmArgs& g, int cfg) {
     if ((g.b_kmajor ? g.K : ci.bn) * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
     if (g.a_kmajor && (!g.b_kmajor || g.epi != kEpiStore)) return false;
     if (g.b_kmajor && ((g.epi != kEpiStore && g.epi != kEpiGeluGrad) || g.ln_mean || g.preact_out)) return false;
+    // the GeLU-derivative epilogue is built for the dS GEMM's layout only
+    // (Bop, the packed B^T, read K-major); anything else takes the generic kernel
+    if (g.epi == kEpiGeluGrad && !g.b_kmajor) return false;
     const int64_t tiles = ((g.M + ci.bm - 1) / ci.bm) * ((g.N + ci.bn - 1) / ci.bn);
     if (tiles * 8 >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) || g.N >= ((int64_t)1 << 31) ||
         g.K >= ((int64_t)1 << 31))
@@ -943,9 +959,7 @@ static hipError_t launch_rowmajor(const GemmArgs& g, int cfg, hipStream_t stream
     if (g.epi == kEpiGelu)
         return g.preact_out ? launch_typed<C, kEpiGeluSave, bf16>(g, 1, stream)
                             : launch_typed<C, kEpiGelu, bf16>(g, 1, stream);
-    if (g.epi == kEpiGeluGrad)
-        return g.gelu_out ? launch_typed<C, kEpiGeluGradSave, bf16>(g, 1, stream)
-                          : launch_typed<C, kEpiGeluGrad, bf16>(g, 1, stream);
+    if (g.epi != kEpiStore) return hipErrorInvalidValue;  // fits_cfg admits no other
     return launch_store<C, 0>(g, cfg, stream);
 }
 

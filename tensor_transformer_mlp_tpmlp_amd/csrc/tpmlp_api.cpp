@@ -299,7 +299,7 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
     if (M == 0) return TPMLP_OK;
     if (!X || !Y) return TPMLP_ERR_NULL;
     if (!aligned16(X) || !aligned16(Y) || (o.residual && !aligned16(o.residual)) ||
-        (o.save_preact && !aligned16(o.save_preact)))
+        (o.save_preact && !aligned16(o.save_preact)) || (o.save_act && !aligned16(o.save_act)))
         return TPMLP_ERR_ALIGN;
 
     const bool single = o.shard_index >= 0;
@@ -323,7 +323,7 @@ tpmlp_status tpmlp_forward_ex(const void* X, int64_t M, const tpmlp_shards* s, v
     const char* bt = at + round_up((size_t)D * (size_t)F * eb);
     const float* csum = reinterpret_cast<const float*>(bt + round_up((size_t)D * (size_t)F * eb));
     char* wsb = static_cast<char*>(ws);
-    void* H = wsb + L.h_off;
+    void* H = o.save_act ? o.save_act : wsb + L.h_off;  // the caller keeps H, or the workspace holds it
     float* mean = ln ? reinterpret_cast<float*>(wsb + L.mean_off) : nullptr;
     float* rstd = ln ? reinterpret_cast<float*>(wsb + L.rstd_off) : nullptr;
 
@@ -384,12 +384,13 @@ size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M) {
 }
 
 tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpmlp_shards* s, const void* preact,
-                            void* dX, void* dA, void* dB, void* workspace, size_t workspace_bytes, void* stream) {
+                            const void* act, void* dX, void* dA, void* dB, void* workspace, size_t workspace_bytes,
+                            void* stream) {
     if (!s) return TPMLP_ERR_NULL;
     if (M < 0 || M > kMaxDim) return TPMLP_ERR_SHAPE;
     if (!dA || !dB || (M > 0 && (!X || !dY || !dX))) return TPMLP_ERR_NULL;
     if (!aligned16(dA) || !aligned16(dB) || (M > 0 && (!aligned16(X) || !aligned16(dY) || !aligned16(dX))) ||
-        (preact && !aligned16(preact)))
+        (preact && !aligned16(preact)) || (act && !aligned16(act)))
         return TPMLP_ERR_ALIGN;
     const BwdLayout L = bwd_layout(s, M);
     if (!workspace || workspace_bytes < L.total) return TPMLP_ERR_WORKSPACE;
@@ -421,10 +422,12 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
     BwdPtrs q;
     q.X = X; q.dY = dY; q.at = at; q.bt = bt;
     q.S = preact ? preact : static_cast<const void*>(w + L.s);
-    q.H = w + L.h; q.dS = w + L.ds;
+    q.H = act ? const_cast<void*>(act) : static_cast<void*>(w + L.h);
+    q.dS = w + L.ds;
     q.dX = dX; q.dA = dA; q.dB = dB;
     auto gemm = [&](int which) {
         GemmArgs g = bwd_args(s, M, which, q);
+        if (which == kBwdDS && act) g.gelu_out = nullptr;  // H is the forward's
         g.split_ws = w + L.split;
         g.split_ws_bytes = L.split_bytes;
         return launch_gemm(g, hs);
@@ -434,7 +437,8 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
     // S = X A for all shards at once, unless the forward kept it
     if (!preact) e = gemm(kBwdS);
     // dS = (dY B^T) * GeLU'(S), the gradient at every shard's GeLU input; the
-    // epilogue that reads S also writes H = GeLU(S) for dB
+    // epilogue that reads S also writes H = GeLU(S) for dB, unless the
+    // forward kept H
     if (e == hipSuccess) e = gemm(kBwdDS);
     // dX = sum_i dS_i A_i^T: the K loop over F sums the shards in registers
     if (e == hipSuccess) e = gemm(kBwdDX);

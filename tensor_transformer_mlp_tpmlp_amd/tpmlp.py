@@ -39,7 +39,8 @@ class Opts(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_int), ("ln_eps", ctypes.c_float), ("y_dtype", ctypes.c_int),
                 ("residual", ctypes.c_void_p), ("shard_index", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("events", ctypes.c_void_p), ("save_preact", ctypes.c_void_p)]
+                ("events", ctypes.c_void_p), ("save_preact", ctypes.c_void_p),
+                ("save_act", ctypes.c_void_p)]
 
 
 SIGNATURES = {
@@ -61,7 +62,8 @@ SIGNATURES = {
     "tpmlp_forward_ex": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, ctypes.POINTER(Opts), _c_vp]),
     "tpmlp_forward_noalloc": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, ctypes.POINTER(Opts), _c_vp]),
     "tpmlp_backward_workspace_bytes": (_c_sz, [_c_vp, _c_i64]),
-    "tpmlp_backward": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "tpmlp_backward": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
+                                _c_vp]),
     "tpmlp_attn_pack_bytes": (_c_sz, [_c_i64, _c_int, _c_int, _c_int, _c_int]),
     "tpmlp_attn_pack": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_sz,
                                  ctypes.POINTER(_c_vp), _c_vp]),
@@ -227,7 +229,8 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, layernor
            residual: Optional[torch.Tensor] = None, shard_index: int = -1,
            out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
            events: Optional[Sequence[int]] = None,
-           save_preact: Optional[torch.Tensor] = None) -> torch.Tensor:
+           save_preact: Optional[torch.Tensor] = None,
+           save_act: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = sum_i GeLU(X A_i) B_i on the GPU (tpmlp_forward_ex).
 
     layernorm: normalise each row of X first (no affine); layernorm_after:
@@ -235,7 +238,9 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, layernor
     after the shard sum; shard_index: return only partial Y_i; events: four
     hipEvent_t handles recorded around the kernels (timing hook);
     save_preact: an (M, F) tensor (F/n with shard_index) of the weights'
-    dtype that receives the pre-activation X A for tp_mlp_backward.
+    dtype that receives the pre-activation X A for tp_mlp_backward;
+    save_act: the same for the activation H = GeLU(X A) (GEMM1 writes it
+    there instead of into the workspace).
     """
     if X.dim() != 2 or X.shape[1] != shards.D:
         raise ValueError(f"X must be (M, {shards.D})")
@@ -267,6 +272,11 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, layernor
         if save_preact.dtype != shards.dtype or tuple(save_preact.shape) != (M, nh):
             raise ValueError(f"save_preact must be ({M}, {nh}) with the weights' dtype")
         o.save_preact = _dev(save_preact, "save_preact")
+    if save_act is not None:
+        nh = shards.F // shards.n if shard_index >= 0 else shards.F
+        if save_act.dtype != shards.dtype or tuple(save_act.shape) != (M, nh):
+            raise ValueError(f"save_act must be ({M}, {nh}) with the weights' dtype")
+        o.save_act = _dev(save_act, "save_act")
     o.workspace = ws.data_ptr()
     o.workspace_bytes = ws.numel()
     ev_arr = None
@@ -280,13 +290,14 @@ def tp_mlp(X: torch.Tensor, shards: Shards, *, layernorm: bool = False, layernor
 
 
 def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards, out=None,
-                    preact: Optional[torch.Tensor] = None):
+                    preact: Optional[torch.Tensor] = None, act: Optional[torch.Tensor] = None):
     """Gradients (dX, dA, dB) of the TP-MLP given dY = dL/dY (tpmlp_backward).
 
     dA has A's layout (D x F, shard i in its columns), dB has B's (F x D,
     shard i in its rows); all three in the weights' dtype.  `out` may give
     the three result tensors; `preact` the (M, F) pre-activation a forward
-    kept with save_preact (otherwise it is recomputed).
+    kept with save_preact (otherwise it is recomputed); `act` the (M, F)
+    activation it kept with save_act (otherwise recomputed from preact).
     """
     if X.dim() != 2 or X.shape[1] != shards.D:
         raise ValueError(f"X must be (M, {shards.D})")
@@ -309,12 +320,17 @@ def tp_mlp_backward(X: torch.Tensor, dY: torch.Tensor, shards: Shards, out=None,
         if preact.dtype != shards.dtype or tuple(preact.shape) != (M, shards.F):
             raise ValueError(f"preact must be ({M}, {shards.F}) with the weights' dtype")
         pp = _dev(preact, "preact") if M else None
+    ap = None
+    if act is not None:
+        if act.dtype != shards.dtype or tuple(act.shape) != (M, shards.F):
+            raise ValueError(f"act must be ({M}, {shards.F}) with the weights' dtype")
+        ap = _dev(act, "act") if M else None
     L = lib()
     nbytes = L.tpmlp_backward_workspace_bytes(shards.handle, M)
     stream = _stream(X.device)
     ws = shards.workspace(nbytes, stream)
     _check(L.tpmlp_backward(_dev(X, "X") if M else X.data_ptr(), _dev(dY, "dY") if M else dY.data_ptr(), M,
-                            shards.handle, pp, _dev(dX, "dX") if M else dX.data_ptr(), _dev(dA, "dA"),
+                            shards.handle, pp, ap, _dev(dX, "dX") if M else dX.data_ptr(), _dev(dA, "dA"),
                             _dev(dB, "dB"), ws.data_ptr(), ws.numel(), stream), "tpmlp_backward")
     return dX, dA, dB
 

@@ -111,7 +111,7 @@ def test_descriptor_functions_reject_null(L):
     assert L.tpmlp_forward(FAKE, 4, None, FAKE, None) == NULL
     assert L.tpmlp_forward_ex(FAKE, 4, None, FAKE, None, None) == NULL
     assert L.tpmlp_backward_workspace_bytes(None, 16) == 0
-    assert L.tpmlp_backward(FAKE, FAKE, 4, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == NULL
+    assert L.tpmlp_backward(FAKE, FAKE, 4, None, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == NULL
     L.tpmlp_shards_destroy(None)  # must be a no-op
 
 

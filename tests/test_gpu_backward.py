@@ -133,14 +133,16 @@ def test_backward_errors_with_real_descriptor():
     need = L.tpmlp_backward_workspace_bytes(sh.handle, 64)
     assert need > 0
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    args = (X.data_ptr(), tdY.data_ptr(), 64, sh.handle, None, dX.data_ptr(), dA.data_ptr(), dB.data_ptr())
+    args = (X.data_ptr(), tdY.data_ptr(), 64, sh.handle, None, None, dX.data_ptr(), dA.data_ptr(), dB.data_ptr())
     assert L.tpmlp_backward(*args, ws.data_ptr(), need - 1, None) == 5      # workspace too small
     assert L.tpmlp_backward(*args, None, need, None) == 5
-    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), -1, sh.handle, None, dX.data_ptr(), dA.data_ptr(),
+    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), -1, sh.handle, None, None, dX.data_ptr(), dA.data_ptr(),
                             dB.data_ptr(), ws.data_ptr(), need, None) == 2
-    assert L.tpmlp_backward(X.data_ptr() + 4, tdY.data_ptr(), 64, sh.handle, None, dX.data_ptr(), dA.data_ptr(),
-                            dB.data_ptr(), ws.data_ptr(), need, None) == 6
-    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), 64, sh.handle, None, dX.data_ptr(), None,
+    assert L.tpmlp_backward(X.data_ptr() + 4, tdY.data_ptr(), 64, sh.handle, None, None, dX.data_ptr(),
+                            dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), need, None) == 6
+    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), 64, sh.handle, None, X.data_ptr() + 4, dX.data_ptr(),
+                            dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), need, None) == 6   # act misaligned
+    assert L.tpmlp_backward(X.data_ptr(), tdY.data_ptr(), 64, sh.handle, None, None, dX.data_ptr(), None,
                             dB.data_ptr(), ws.data_ptr(), need, None) == 1
     assert L.tpmlp_backward(*args, ws.data_ptr(), need, None) == 0
     torch.cuda.synchronize()
@@ -171,3 +173,35 @@ def test_forward_saves_preact_and_backward_uses_it(M, D, F, n, dtype):
     torch.cuda.synchronize()
     for a, b in zip(with_s, without):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("M,D,F,n,dtype", [(512, 256, 1024, 4, "bf16"), (1024, 512, 2048, 2, "bf16"),
+                                           (130, 70, 96, 3, "f32")])
+def test_backward_with_kept_activation(M, D, F, n, dtype):
+    """A forward that keeps S (save_preact) and H (save_act): the kept H is
+    GeLU of the oracle's S to the dtype's tolerance, the forward's Y is
+    unchanged by keeping it, and a backward given both matches the oracle
+    gradients.  Its dX and dA are bit-identical to those of the backward that
+    recomputes H (they do not read H); dB uses the forward's H, which was
+    rounded once from fp32 rather than from the rounded S."""
+    say(f"save_act M={M} D={D} F={F} n={n} {dtype}")
+    inp, dY = _case(M, D, F, seed=5151 + M, dtype=dtype)
+    dt = torch_dtype(dtype)
+    X, A, B, tdY = (to_dev(a, dt) for a in (inp.X, inp.A, inp.B, dY))
+    sh = tp.shard_mlp(A, B, n)
+    S = torch.full((M, F), float("nan"), dtype=dt, device="cuda")
+    H = torch.full((M, F), float("nan"), dtype=dt, device="cuda")
+    Y = tp.tp_mlp(X, sh, save_preact=S, save_act=H)
+    Y0 = tp.tp_mlp(X, sh)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y0)
+    s_ref = inp.X.astype(np.float64) @ inp.A.astype(np.float64)
+    assert_close(to_f64(H), oracle.gelu(s_ref), dtype, "kept activation")
+    kept = tp.tp_mlp_backward(X, tdY, sh, preact=S, act=H)
+    torch.cuda.synchronize()
+    rebuilt = tp.tp_mlp_backward(X, tdY, sh, preact=S)
+    torch.cuda.synchronize()
+    assert torch.equal(kept[0], rebuilt[0]) and torch.equal(kept[1], rebuilt[1])
+    rX, rA, rB = oracle.tp_mlp_backward_full(inp.X, inp.A, inp.B, n, dY)
+    for got, ref, nm in zip(kept, (rX, rA, rB), ("dX", "dA", "dB")):
+        assert_close(to_f64(got), ref, dtype, nm + " (kept H)")
