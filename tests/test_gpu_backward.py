@@ -205,3 +205,35 @@ def test_backward_with_kept_activation(M, D, F, n, dtype):
     rX, rA, rB = oracle.tp_mlp_backward_full(inp.X, inp.A, inp.B, n, dY)
     for got, ref, nm in zip(kept, (rX, rA, rB), ("dX", "dA", "dB")):
         assert_close(to_f64(got), ref, dtype, nm + " (kept H)")
+
+
+def test_kept_activation_of_one_shard_and_alignment():
+    """save_act with shard_index = i receives GPU i's H_i (M x F/n), the same
+    values as columns iF/n .. (i+1)F/n - 1 of the all-shards H; its partial
+    Y_i is unchanged by keeping it; a misaligned save_act is TPMLP_ERR_ALIGN
+    before any work."""
+    import ctypes
+    M, D, F, n = 512, 256, 1024, 4
+    say(f"save_act with shard_index M={M} D={D} F={F} n={n}")
+    inp, _ = _case(M, D, F, seed=6161, dtype="bf16")
+    X, A, B = (to_dev(a, torch.bfloat16) for a in (inp.X, inp.A, inp.B))
+    sh = tp.shard_mlp(A, B, n)
+    H = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    tp.tp_mlp(X, sh, save_act=H)
+    w = F // n
+    for i in (0, n - 1):
+        Hi = torch.full((M, w), float("nan"), dtype=torch.bfloat16, device="cuda")
+        Yi = tp.tp_mlp(X, sh, shard_index=i, save_act=Hi)
+        Yi0 = tp.tp_mlp(X, sh, shard_index=i)
+        torch.cuda.synchronize()
+        assert torch.equal(Hi, H[:, i * w:(i + 1) * w])
+        assert torch.equal(Yi, Yi0)
+    L = tp.lib()
+    need = L.tpmlp_forward_workspace_bytes(sh.handle, M, 0, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    Y = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    o = tp.tpmlp.Opts()
+    L.tpmlp_opts_init(ctypes.byref(o))
+    o.workspace, o.workspace_bytes = ws.data_ptr(), ws.numel()
+    o.save_act = H.data_ptr() + 4
+    assert L.tpmlp_forward_ex(X.data_ptr(), M, sh.handle, Y.data_ptr(), ctypes.byref(o), None) == 6
