@@ -84,7 +84,8 @@ const char* tpmlp_version(void);
 tpmlp_status tpmlp_gelu(const void* x, void* y, int64_t count, int dtype, void* stream);
 
 /*
- * Bytes of the packed weight buffer tpmlp_shard needs for (D, F, n, dtype);
+ * Bytes of the packed weight buffer tpmlp_shard needs for (D, F, n, dtype):
+ * four D x F matrices and F floats, each segment rounded up to 256 bytes;
  * 0 if the arguments are invalid.
  */
 size_t tpmlp_shard_bytes(int64_t D, int64_t F, int n, int dtype);
@@ -99,9 +100,11 @@ size_t tpmlp_shard_bytes(int64_t D, int64_t F, int n, int dtype);
  *   packed  device buffer of at least tpmlp_shard_bytes(D, F, n, dtype)
  *           bytes, owned by the caller, which must keep it alive and
  *           unmodified while the returned descriptor is in use.  The pairs are
- *           stored K-contiguous for the matrix cores (A_i transposed to
- *           F/n x D, B transposed to D x F); A and B may be released once the
- *           work enqueued on `stream` has completed.
+ *           stored K-contiguous for the forward's matrix-core GEMMs (A_i
+ *           transposed to F/n x D, B transposed to D x F), with the column
+ *           sums of A, followed by copies of A and B as given, which are the
+ *           K-contiguous operands of the backward's dX and dS GEMMs.  A and B
+ *           may be released once the work enqueued on `stream` has completed.
  *   out     receives a new host descriptor (set to NULL on error).
  * Errors: TPMLP_ERR_NULL, TPMLP_ERR_SHAPE (D <= 0, F <= 0, n <= 0, n > F,
  * a dimension above 2^21), TPMLP_ERR_INDIVISIBLE

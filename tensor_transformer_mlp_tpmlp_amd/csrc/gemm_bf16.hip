@@ -792,9 +792,6 @@ static bool fits_cfg(const GemmArgs& g, int cfg) {
     if ((g.b_kmajor ? g.K : ci.bn) * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
     if (g.a_kmajor && (!g.b_kmajor || g.epi != kEpiStore)) return false;
     if (g.b_kmajor && ((g.epi != kEpiStore && g.epi != kEpiGeluGrad) || g.ln_mean || g.preact_out)) return false;
-    // the GeLU-derivative epilogue is built for the dS GEMM's layout only
-    // (Bop, the packed B^T, read K-major); anything else takes the generic kernel
-    if (g.epi == kEpiGeluGrad && !g.b_kmajor) return false;
     const int64_t tiles = ((g.M + ci.bm - 1) / ci.bm) * ((g.N + ci.bn - 1) / ci.bn);
     if (tiles * 8 >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) || g.N >= ((int64_t)1 << 31) ||
         g.K >= ((int64_t)1 << 31))
@@ -959,7 +956,9 @@ static hipError_t launch_rowmajor(const GemmArgs& g, int cfg, hipStream_t stream
     if (g.epi == kEpiGelu)
         return g.preact_out ? launch_typed<C, kEpiGeluSave, bf16>(g, 1, stream)
                             : launch_typed<C, kEpiGelu, bf16>(g, 1, stream);
-    if (g.epi != kEpiStore) return hipErrorInvalidValue;  // fits_cfg admits no other
+    if (g.epi == kEpiGeluGrad)
+        return g.gelu_out ? launch_typed<C, kEpiGeluGradSave, bf16>(g, 1, stream)
+                          : launch_typed<C, kEpiGeluGrad, bf16>(g, 1, stream);
     return launch_store<C, 0>(g, cfg, stream);
 }
 

@@ -78,13 +78,13 @@ WsLayout ws_layout(const tpmlp_shards* s, int64_t M, int flags, int single_shard
 // operand read where it lies (K-major where the contraction runs over its
 // rows), so nothing is transposed:
 //   S  = X A:     Aop = X (M x D),          Bop = A^T, packed (F x D)
-//   dS = dY B^T:  Aop = dY (M x D),         Bop = B, i.e. the packed B^T (D x F) read K-major
-//   dX = dS A^T:  Aop = dS (M x F),         Bop = A, i.e. the packed A^T (F x D) read K-major
+//   dS = dY B^T:  Aop = dY (M x D),         Bop = B (F x D), the packed copy as given
+//   dX = dS A^T:  Aop = dS (M x F),         Bop = A (D x F), the packed copy as given
 //   dA = X^T dS:  Aop = X^T: X read K-major, Bop = dS^T: dS read K-major   (K = M)
 //   dB = H^T dY:  Aop = H^T: H read K-major, Bop = dY^T: dY read K-major   (K = M)
 enum { kBwdS, kBwdDS, kBwdDX, kBwdDA, kBwdDB };
 struct BwdPtrs {
-    const void *X, *dY, *at, *bt, *S;
+    const void *X, *dY, *at, *a, *b, *S;
     void *H, *dS, *dX, *dA, *dB;
 };
 
@@ -101,13 +101,13 @@ GemmArgs bwd_args(const tpmlp_shards* s, int64_t M, int which, const BwdPtrs& q)
             g.M = M; g.N = F; g.K = D; g.C = const_cast<void*>(q.S); g.ldc = F;
             break;
         case kBwdDS:
-            g.A = q.dY; g.lda = D; g.B = q.bt; g.ldb = F; g.b_kmajor = true;
+            g.A = q.dY; g.lda = D; g.B = q.b; g.ldb = D;
             g.M = M; g.N = F; g.K = D; g.C = q.dS; g.ldc = F;
             g.epi = kEpiGeluGrad; g.aux = q.S; g.ldaux = F;
             g.gelu_out = q.H;
             break;
         case kBwdDX:
-            g.A = q.dS; g.lda = F; g.B = q.at; g.ldb = D; g.b_kmajor = true;
+            g.A = q.dS; g.lda = F; g.B = q.a; g.ldb = F;
             g.M = M; g.N = D; g.K = F; g.C = q.dX; g.ldc = D;
             break;
         case kBwdDA:
@@ -184,9 +184,30 @@ tpmlp_status tpmlp_gelu(const void* x, void* y, int64_t count, int dtype, void* 
     return from_hip(launch_gelu(x, y, count, dtype, static_cast<hipStream_t>(stream)));
 }
 
+// Packed weight buffer, each segment 256-byte aligned:
+//   A^T (F x D) and B^T (D x F): the forward's K-contiguous operands, pair i
+//     in rows (columns) iF/n..(i+1)F/n-1;
+//   F fp32 column sums of A (the LayerNorm epilogue);
+//   A (D x F) and B (F x D) as given: K-contiguous operands of the backward's
+//     dX = dS A^T and dS = dY B^T GEMMs.
+struct PackLayout {
+    size_t at, bt, csum, a, b, total;
+};
+PackLayout pack_layout(int64_t D, int64_t F, int dtype) {
+    const size_t w = round_up((size_t)D * (size_t)F * elem_size(dtype));
+    PackLayout L;
+    L.at = 0;
+    L.bt = w;
+    L.csum = 2 * w;
+    L.a = L.csum + round_up((size_t)F * 4);
+    L.b = L.a + w;
+    L.total = L.b + w;
+    return L;
+}
+
 size_t tpmlp_shard_bytes(int64_t D, int64_t F, int n, int dtype) {
     if (check_shard_args(D, F, n, dtype) != TPMLP_OK) return 0;
-    return round_up((size_t)D * (size_t)F * elem_size(dtype)) * 2 + round_up((size_t)F * 4);
+    return pack_layout(D, F, dtype).total;
 }
 
 tpmlp_status tpmlp_shard(const void* A, const void* B, int64_t D, int64_t F, int n, int dtype,
@@ -211,15 +232,21 @@ tpmlp_status tpmlp_shard(const void* A, const void* B, int64_t D, int64_t F, int
 
     // Pair i of "The split" is rows iF/n..(i+1)F/n-1 of A^T and columns
     // iF/n..(i+1)F/n-1 of B^T: one transpose of each matrix packs all pairs,
-    // each K-contiguous for the matrix cores.
+    // each K-contiguous for the matrix cores.  A and B are also kept as
+    // given, the K-contiguous operands of the backward's dX and dS GEMMs.
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int eb = (int)elem_size(dtype);
-    char* at = static_cast<char*>(packed);
-    char* bt = at + round_up((size_t)D * (size_t)F * eb);
-    float* csum = reinterpret_cast<float*>(bt + round_up((size_t)D * (size_t)F * eb));
+    const PackLayout P = pack_layout(D, F, dtype);
+    char* base = static_cast<char*>(packed);
+    char* at = base + P.at;
+    char* bt = base + P.bt;
+    float* csum = reinterpret_cast<float*>(base + P.csum);
+    const size_t bytes = (size_t)D * (size_t)F * eb;
     hipError_t e = launch_transpose(A, F, at, D, D, F, eb, hs);        // A (D x F) -> A^T (F x D)
     if (e == hipSuccess) e = launch_transpose(B, D, bt, F, F, D, eb, hs);  // B (F x D) -> B^T (D x F)
     if (e == hipSuccess) e = launch_rowsum(at, F, D, dtype, csum, hs);  // column sums of A
+    if (e == hipSuccess) e = hipMemcpyAsync(base + P.a, A, bytes, hipMemcpyDeviceToDevice, hs);
+    if (e == hipSuccess) e = hipMemcpyAsync(base + P.b, B, bytes, hipMemcpyDeviceToDevice, hs);
     if (e != hipSuccess) {
         delete s;
         return TPMLP_ERR_HIP;
@@ -400,8 +427,8 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
     const int dt = s->dtype;
     const int eb = (int)elem_size(dt);
     const int64_t D = s->D, F = s->F;
-    const char* at = static_cast<const char*>(s->packed);                     // A^T: F x D
-    const char* bt = at + round_up((size_t)D * (size_t)F * eb);              // B^T: D x F
+    const PackLayout P = pack_layout(D, F, dt);
+    const char* pk = static_cast<const char*>(s->packed);
     char* w = static_cast<char*>(workspace);
 
     if (M == 0) {
@@ -420,7 +447,10 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
     }
 
     BwdPtrs q;
-    q.X = X; q.dY = dY; q.at = at; q.bt = bt;
+    q.X = X; q.dY = dY;
+    q.at = pk + P.at;   // A^T (F x D)
+    q.a = pk + P.a;     // A (D x F)
+    q.b = pk + P.b;     // B (F x D)
     q.S = preact ? preact : static_cast<const void*>(w + L.s);
     q.H = act ? const_cast<void*>(act) : static_cast<void*>(w + L.h);
     q.dS = w + L.ds;

@@ -69,9 +69,10 @@ def test_gelu_validation(L):
 
 def test_shard_bytes(L):
     # A^T and B^T, each rounded up to 256 bytes, then F fp32 column sums
-    assert L.tpmlp_shard_bytes(2, 4, 2, 0) == 3 * 256
-    assert L.tpmlp_shard_bytes(4096, 16384, 8, 1) == 2 * 4096 * 16384 * 2 + 16384 * 4
-    assert L.tpmlp_shard_bytes(3, 5, 1, 0) == 3 * 256
+    # A^T, B^T, the column sums of A, then A and B as given: 256-byte segments
+    assert L.tpmlp_shard_bytes(2, 4, 2, 0) == 5 * 256
+    assert L.tpmlp_shard_bytes(4096, 16384, 8, 1) == 4 * 4096 * 16384 * 2 + 16384 * 4
+    assert L.tpmlp_shard_bytes(3, 5, 1, 0) == 5 * 256
     for bad in [(0, 4, 2, 0), (2, 0, 1, 0), (2, 4, 3, 0), (2, 4, 0, 0), (2, 4, 8, 0), (2, 4, 2, 9)]:
         assert L.tpmlp_shard_bytes(*bad) == 0
 
