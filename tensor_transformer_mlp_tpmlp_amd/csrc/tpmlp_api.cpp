@@ -142,7 +142,7 @@ BwdLayout bwd_layout(const tpmlp_shards* s, int64_t M) {
         // the split plan depends on shapes, leading dimensions and layouts, not
         // on addresses: aligned stand-ins
         char* const fake = reinterpret_cast<char*>((uintptr_t)256);
-        const BwdPtrs q{fake, fake, fake, fake, fake, fake, fake, fake, fake, fake};
+        const BwdPtrs q{fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake};
         for (int which = kBwdS; which <= kBwdDB; ++which) {
             const size_t c = gemm_split_bytes(bwd_args(s, M, which, q));
             sb = c > sb ? c : sb;
@@ -425,7 +425,6 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int dt = s->dtype;
-    const int eb = (int)elem_size(dt);
     const int64_t D = s->D, F = s->F;
     const PackLayout P = pack_layout(D, F, dt);
     const char* pk = static_cast<const char*>(s->packed);
