@@ -89,6 +89,25 @@ __device__ __forceinline__ void dma16_asm(uint8_t* dst, u32x4 r, uint32_t voff, 
                  : "memory");
 }
 
+// One 16-byte-per-lane direct load from global memory into LDS: lane L's 16
+// bytes at base + voff land at LDS byte address lds + 16 L (lds wave-uniform,
+// an LDS address rather than a pointer, which the compiler would convert
+// with a null check on every load).  base is wave-uniform (a scalar
+// register pair), voff a per-lane 32-bit offset; there is no range check, so
+// every address must lie inside the operand.  On gfx950 this form disturbs
+// the matrix pipe much less than the buffer form: in a stream of 16x16x32
+// MFMAs, one every eight MFMAs costs about 12 cycles against about 23-28.
+// Like dma16_asm it is written out (the compiler sees no LDS write in
+// flight) and needs one wait state after the M0 write.
+__device__ __forceinline__ void gdma16_asm(uint32_t lds, const void* base, uint32_t voff) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"{m0}"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+// The LDS byte address of a __shared__ object, as a wave-uniform value.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+
 // Transposing LDS read of four 16-bit values (ds_read_b64_tr_b16).  Within
 // each group of 16 lanes, lane i supplies the address of 4 consecutive
 // elements (row i / 4 of a 4 x 16 block when the addresses are set up as

@@ -253,22 +253,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     const int kc = p.K / p.splits;      // this block's K range: [kz kc, (kz+1) kc)
     const int64_t k0 = (int64_t)kz * kc;
 
-    // Buffer resources over this tile's rows of each operand, from its K range
-    // on; a K-major operand's resource starts at row k0, column m0 (n0) and
-    // runs to the end of the operand.  (K-major operands come in whole tiles.)
-    const int64_t rows_a = min((int64_t)BM, (int64_t)p.M - m0), rows_b = min((int64_t)BN, (int64_t)p.N - n0);
-    const uint32_t a_bytes = KA ? (uint32_t)((p.K - k0) * p.lda * 2 - m0 * 2) : (uint32_t)(rows_a * p.lda * 2 - k0 * 2);
-    const uint32_t b_bytes = KB ? (uint32_t)((p.K - k0) * p.ldb * 2 - n0 * 2) : (uint32_t)(rows_b * p.ldb * 2 - k0 * 2);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(KA ? p.A + k0 * p.lda + m0 : p.A + m0 * p.lda + k0), (short)0, (int)a_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(KB ? p.B + k0 * p.ldb + n0 : p.B + n0 * p.ldb + k0), (short)0, (int)b_bytes, 0x00020000);
-    // The same with no records: every load through it is out of range, reads
-    // no memory and writes zeros to LDS.  The ring issues its last units
-    // through these (see the main loop).
-    const __amdgpu_buffer_rsrc_t ra0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(p.A), (short)0, 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(p.B), (short)0, 0, 0x00020000);
-
+    // This tile's panel of each operand from its K range on: a row-major
+    // operand's row m0 (n0) at column k0, a K-major operand's row k0 at
+    // column m0 (n0).  A K-loop load of step ks reads panel + ks * step plus
+    // a per-lane offset, with ks clamped to the range's last step and the
+    // rows of a row-major operand clamped to the operand, so every load
+    // reads inside the operand.  (K is a whole number of steps; K-major
+    // operands come in whole tiles.)
+    const uint8_t* const pan_a = reinterpret_cast<const uint8_t*>(KA ? p.A + k0 * p.lda + m0 : p.A + m0 * p.lda + k0);
+    const uint8_t* const pan_b = reinterpret_cast<const uint8_t*>(KB ? p.B + k0 * p.ldb + n0 : p.B + n0 * p.ldb + k0);
+    const uint64_t step_a = KA ? (uint64_t)BK * (uint64_t)p.lda * 2 : (uint64_t)BK * 2;
+    const uint64_t step_b = KB ? (uint64_t)BK * (uint64_t)p.ldb * 2 : (uint64_t)BK * 2;
+    const int nk = kc / BK;   // >= 1
     // row-major operands: per-load lane offsets (rows clamped to the operand)
     uint32_t va[KA ? 1 : LPA], vb[KB ? 1 : LPB];
     if constexpr (!KA) row_load_offsets<BM, LPA>(va, w, lane, m0, p.M, p.lda);
@@ -277,15 +273,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
 
     // slot s of the ring
     auto slot = [&](int s) { return ring + s * SLOT; };
-
-    // the same resources as SGPR dwords for the inline-assembly loads
-    u32x4 ra4 = {}, rb4 = {}, ra40 = {}, rb40 = {};
-    if constexpr (KM != 0) {
-        ra4 = buffer_rsrc_sgpr(KA ? p.A + k0 * p.lda + m0 : p.A + m0 * p.lda + k0, a_bytes);
-        rb4 = buffer_rsrc_sgpr(KB ? p.B + k0 * p.ldb + n0 : p.B + n0 * p.ldb + k0, b_bytes);
-        ra40 = buffer_rsrc_sgpr(p.A, 0u);
-        rb40 = buffer_rsrc_sgpr(p.B, 0u);
-    }
 
     // K-major operand units: 64 rows (k) of 2 BM (2 BN) bytes (the tile's
     // columns), 16-byte chunk c of row r at physical chunk c ^ kswz(r).  Wave
@@ -310,25 +297,23 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     }
 
     // load q of the unit of operand `op` (0 = Aop, 1 = Bop) of K step kstep
-    // into slot st, through the empty resource when !real (with a K-major
-    // operand every load goes through dma16_asm, since the transposing reads
-    // would wait for any direct load the compiler sees)
-    auto load_one = [&](uint8_t* st, int op, int kstep, int q, bool real) {
-        const uint32_t kb = (uint32_t)kstep * (uint32_t)(BK * 2);
-        uint32_t voff, soff;
-        uint8_t* dst;
+    // into slot st; a step past the range's last reloads the last one (see
+    // the main loop)
+    const uint32_t ring_lds = lds_addr(ring);
+    auto load_one = [&](uint8_t* st, int op, int kstep, int q) {
+        const uint64_t ks = (uint64_t)(kstep < nk ? kstep : nk - 1);
+        const uint32_t sl = ring_lds + (uint32_t)(st - ring);
         if (op) {
-            dst = st + dst_b + q * 1024;
-            if constexpr (KB) { voff = kv_b[q]; soff = (uint32_t)(kstep * BK) * (uint32_t)(p.ldb * 2); }
-            else { voff = vb[q]; soff = kb; }
+            uint32_t voff;
+            if constexpr (KB) voff = kv_b[q];
+            else voff = vb[q];
+            gdma16_asm(sl + dst_b + q * 1024, pan_b + ks * step_b, voff);
         } else {
-            dst = st + dst_a + q * 1024;
-            if constexpr (KA) { voff = kv_a[q]; soff = (uint32_t)(kstep * BK) * (uint32_t)(p.lda * 2); }
-            else { voff = va[q]; soff = kb; }
+            uint32_t voff;
+            if constexpr (KA) voff = kv_a[q];
+            else voff = va[q];
+            gdma16_asm(sl + dst_a + q * 1024, pan_a + ks * step_a, voff);
         }
-        if constexpr (KM != 0) dma16_asm(dst, op ? (real ? rb4 : rb40) : (real ? ra4 : ra40), voff, soff);
-        else __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? (real ? rb : rb0) : (real ? ra : ra0), (lds_void*)dst, 16,
-                                                      voff, soff, 0, 0);
     };
 
     // MFMA operand reads: a 16x16x32 fragment is 16 rows x 32 k; in sub-step
@@ -401,7 +386,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 
     bf16x8 fa0[NBM], fb0[NBN], fa1[NBM], fb1[NBN];
-    const int nk = kc / BK;   // >= 1
 
     // Per sub-step: NM MFMAs; the NR fragment reads of the next sub-step go
     // one after every RS-th MFMA from the first, the direct loads of one unit
@@ -420,11 +404,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // One sub-step: MFMAs on (fc, gc); read the next fragments at chunk
     // offset ch, sub-step kk, from units ua (Aop) and ub (Bop) into (fn, gn)
     // when do_read; with OP = 0 (1) issue the Aop (Bop) unit of K step ks
-    // into slot dst (through the empty resource when !real), with OP = -1
-    // nothing.
+    // into slot dst, with OP = -1 nothing.
     auto sub_step = [&](const bf16x8 (&fc)[NBM], const bf16x8 (&gc)[NBN], const uint8_t* ua, const uint8_t* ub,
                         uint32_t ch, int kk, bf16x8 (&fn)[NBM], bf16x8 (&gn)[NBN], bool do_read, auto op_c,
-                        uint8_t* dst, int ks, bool real) {
+                        uint8_t* dst, int ks) {
         constexpr int OP = decltype(op_c)::value;
         constexpr int LP = OP == 1 ? LPB : LPA;
         constexpr int LS = NM / LP;
@@ -440,7 +423,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
                 else fn[r - NBN] = frag_a(ua, ch, kk, r - NBN);
             }
             if constexpr (OP >= 0)
-                if (idx % LS == 0) load_one(dst, OP, ks, idx / LS, real);
+                if (idx % LS == 0) load_one(dst, OP, ks, idx / LS);
         }
     };
 
@@ -452,8 +435,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     };
 
     // Units past the last one (u >= 2 nk) are issued like the others but
-    // through the empty resources: they read nothing and fill slots nobody
-    // reads again with zeros.  So every step but the last has the same code
+    // reload the last K step's unit into slots nobody reads again (they are
+    // drained before the epilogue reuses the ring).  So every step but the last has the same code
     // and the same count of loads in flight at its barrier (one loop, whose
     // register assignment stays fixed: two loops let the allocator move an
     // accumulator through VGPRs between the inline-assembly MFMAs, which the
@@ -462,13 +445,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
 #pragma unroll
     for (int u = 0; u < NU - 1; ++u) {
         uint8_t* st = slot(u);
-        const bool real = u < 2 * nk;
         if (u & 1) {
 #pragma unroll
-            for (int q = 0; q < LPB; ++q) load_one(st, 1, u >> 1, q, real);
+            for (int q = 0; q < LPB; ++q) load_one(st, 1, u >> 1, q);
         } else {
 #pragma unroll
-            for (int q = 0; q < LPA; ++q) load_one(st, 0, u >> 1, q, real);
+            for (int q = 0; q < LPA; ++q) load_one(st, 0, u >> 1, q);
         }
     }
     constexpr int VM_PRO = ((NU - 2) / 2) * LPA + ((NU - 3) / 2) * LPB;  // units 2 .. NU-2
@@ -491,17 +473,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     for (int tt = 0; tt < nk - 1; ++tt) {
         const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3), sp = next(sa, NU - 1);
         const int u0 = 2 * tt + NU - 1;
-        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, 1, fa1, fb1, true, ic<OP0>{}, slot(sp), u0 >> 1, u0 < 2 * nk);
+        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, 1, fa1, fb1, true, ic<OP0>{}, slot(sp), u0 >> 1);
         barrier_wait(ic<C::VM_STEADY>{});
-        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, 0, fa0, fb0, true, ic<OP1>{}, slot(sa), (u0 + 1) >> 1,
-                 u0 + 1 < 2 * nk);
+        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, 0, fa0, fb0, true, ic<OP1>{}, slot(sa), (u0 + 1) >> 1);
         sa = sa1;
     }
-    // the last step: nothing left to load or to read ahead; the empty loads
+    // the last step: nothing left to load or to read ahead; the reloads
     // still in flight (the last units of the ring) finish before the epilogue
-    sub_step(fa0, fb0, slot(sa), slot(next(sa, 1)), ch1, 1, fa1, fb1, true, ic<-1>{}, nullptr, 0, false);
+    sub_step(fa0, fb0, slot(sa), slot(next(sa, 1)), ch1, 1, fa1, fb1, true, ic<-1>{}, nullptr, 0);
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
-    sub_step(fa1, fb1, slot(sa), slot(sa), ch0, 0, fa0, fb0, false, ic<-1>{}, nullptr, 0, false);
+    sub_step(fa1, fb1, slot(sa), slot(sa), ch0, 0, fa0, fb0, false, ic<-1>{}, nullptr, 0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     // a bf16 output is staged in the ring's LDS: every wave must be done
     // reading its last units first
