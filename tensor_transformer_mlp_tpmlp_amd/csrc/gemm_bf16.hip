@@ -469,15 +469,49 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // their operands are fixed by the parity of NU.  Every barrier leaves the
     // units 2t+4 .. 2t+NU-1 in flight.
     constexpr int OP0 = (NU - 1) & 1, OP1 = NU & 1;
-    int sa = 0;  // slot of A_t
-    for (int tt = 0; tt < nk - 1; ++tt) {
-        const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3), sp = next(sa, NU - 1);
+    // A_t sits in slot 2t mod NU.  For the 256x256 tile of row-major operands
+    // the loop body is written out for the five phases of that slot (NU = 5)
+    // with the slots as constants, each followed by the exit test: the slot
+    // arithmetic otherwise opens a gap of about 25 scalar instructions in
+    // the MFMA stream at every step.  (Written out for the other tiles, the
+    // register allocator moves accumulators through VGPRs and spills.)
+    auto step = [&](auto sa_c, int tt) {
+        constexpr int SA = decltype(sa_c)::value;
+        constexpr int SB = (SA + 1) % NU, SA1 = (SA + 2) % NU, SB1 = (SA + 3) % NU, SP = (SA + NU - 1) % NU;
         const int u0 = 2 * tt + NU - 1;
-        sub_step(fa0, fb0, slot(sa), slot(sb), ch1, 1, fa1, fb1, true, ic<OP0>{}, slot(sp), u0 >> 1);
+        sub_step(fa0, fb0, slot(SA), slot(SB), ch1, 1, fa1, fb1, true, ic<OP0>{}, slot(SP), u0 >> 1);
         barrier_wait(ic<C::VM_STEADY>{});
-        sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, 0, fa0, fb0, true, ic<OP1>{}, slot(sa), (u0 + 1) >> 1);
-        sa = sa1;
+        sub_step(fa1, fb1, slot(SA1), slot(SB1), ch0, 0, fa0, fb0, true, ic<OP1>{}, slot(SA), (u0 + 1) >> 1);
+    };
+    int tt = 0;
+    if constexpr (KM == 0 && BM == 256 && BN == 256) {
+        static_assert(NU == 5, "five slot phases");
+        if (nk > 1) {
+            for (;;) {
+                step(ic<0>{}, tt);
+                if (++tt == nk - 1) break;
+                step(ic<2>{}, tt);
+                if (++tt == nk - 1) break;
+                step(ic<4>{}, tt);
+                if (++tt == nk - 1) break;
+                step(ic<1>{}, tt);
+                if (++tt == nk - 1) break;
+                step(ic<3>{}, tt);
+                if (++tt == nk - 1) break;
+            }
+        }
+    } else {
+        int sa = 0;  // slot of A_t
+        for (; tt < nk - 1; ++tt) {
+            const int sb = next(sa, 1), sa1 = next(sa, 2), sb1 = next(sa, 3), sp = next(sa, NU - 1);
+            const int u0 = 2 * tt + NU - 1;
+            sub_step(fa0, fb0, slot(sa), slot(sb), ch1, 1, fa1, fb1, true, ic<OP0>{}, slot(sp), u0 >> 1);
+            barrier_wait(ic<C::VM_STEADY>{});
+            sub_step(fa1, fb1, slot(sa1), slot(sb1), ch0, 0, fa0, fb0, true, ic<OP1>{}, slot(sa), (u0 + 1) >> 1);
+            sa = sa1;
+        }
     }
+    const int sa = (2 * tt) % NU;  // slot of A of the last step
     // the last step: nothing left to load or to read ahead; the reloads
     // still in flight (the last units of the ring) finish before the epilogue
     sub_step(fa0, fb0, slot(sa), slot(next(sa, 1)), ch1, 1, fa1, fb1, true, ic<-1>{}, nullptr, 0);

@@ -126,16 +126,25 @@ def test_shapes(M, D, F, n, dtype):
     assert_close(to_f64(Y), oracle_forward(inp.X, inp.A, inp.B, n), dtype, f"M={M} D={D} F={F} n={n}")
 
 
-# The throughput GEMM streams K through a ring of LDS units with its first
-# step and its last two steps peeled, and needs K >= 3 steps of 64.  These
-# shapes put each tile size on the shortest K runs: 256x256 tiles (GEMM1 with
-# M x F = 4096 x 4096, or GEMM2 with M x D = 4096 x 4096) and 128x128 tiles.
+# The throughput GEMM streams K (64-wide steps) through a ring of LDS units
+# with its last step peeled.  For 256x256 tiles of row-major operands the
+# loop body is written out for the five phases of the ring's slots and
+# leaves after any of them, so these shapes run 1 to 7 steps on 256x256
+# tiles (GEMM1 with M x F = 4096 x 4096, or GEMM2 with M x D = 4096 x 4096;
+# the other GEMM is small and takes small tiles) and a short loop on 128x128.
 RING_SHAPES = [
     # (M, D, F, n): which GEMM hits the ring with how many K steps
-    (4096, 192, 4096, 1),   # GEMM1 256x256, 3 steps (GEMM2 N = 192: generic)
+    (4096, 64, 4096, 1),    # GEMM1 256x256, 1 step (no loop)
+    (4096, 128, 4096, 2),   # GEMM1 256x256, 2 steps
+    (4096, 192, 4096, 1),   # GEMM1 256x256, 3 steps
     (4096, 256, 4096, 2),   # GEMM1 256x256, 4 steps
     (4096, 320, 4096, 4),   # GEMM1 256x256, 5 steps
-    (4096, 4096, 192, 1),   # GEMM2 256x256, 3 steps (GEMM1 N = 192: generic)
+    (4096, 384, 4096, 2),   # GEMM1 256x256, 6 steps (one full round of phases)
+    (4096, 448, 4096, 1),   # GEMM1 256x256, 7 steps (into the second round)
+    (4096, 4096, 64, 1),    # GEMM2 256x256, 1 step
+    (4096, 4096, 128, 1),   # GEMM2 256x256, 2 steps
+    (4096, 4096, 192, 1),   # GEMM2 256x256, 3 steps
+    (4096, 4096, 448, 1),   # GEMM2 256x256, 7 steps
     (512, 192, 512, 2),     # GEMM1 128x128, 3 steps
 ]
 
