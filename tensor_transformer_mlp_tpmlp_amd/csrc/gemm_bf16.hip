@@ -436,11 +436,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
 
     // Units past the last one (u >= 2 nk) are issued like the others but
     // reload the last K step's unit into slots nobody reads again (they are
-    // drained before the epilogue reuses the ring).  So every step but the last has the same code
-    // and the same count of loads in flight at its barrier (one loop, whose
-    // register assignment stays fixed: two loops let the allocator move an
-    // accumulator through VGPRs between the inline-assembly MFMAs, which the
-    // compiler cannot pad for).
+    // drained before the epilogue reuses the ring).  So every step but the
+    // last issues the same instructions and has the same count of loads in
+    // flight at its barrier (one loop, whose register assignment stays
+    // fixed: two loops let the allocator move an accumulator through VGPRs
+    // between the inline-assembly MFMAs, which the compiler cannot pad for).
     // prologue: units 0 .. NU-2; wait for A_0 and B_0
 #pragma unroll
     for (int u = 0; u < NU - 1; ++u) {
