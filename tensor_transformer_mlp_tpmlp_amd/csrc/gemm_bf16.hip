@@ -28,10 +28,12 @@
 // accumulators are four consecutive output columns of one row: the epilogue
 // writes 8 (bf16) or 16 (fp32) contiguous bytes per lane and block.
 //
-// Global -> LDS moves use the direct-to-LDS buffer load (buffer_load_dwordx4
-// ... lds): no VGPR staging and no ds_write.  Lane L of a wave's load lands at
-// LDS base + 16 L, so the XOR swizzle of the LDS layout is applied on the
-// global side by choosing which 16-byte chunk each lane fetches.
+// Global -> LDS moves use the direct-to-LDS global load
+// (global_load_lds_dwordx4, a scalar base and 32-bit lane offsets): no VGPR
+// staging and no ds_write, and in the MFMA stream about half the issue cost
+// of the buffer form.  Lane L of a wave's load lands at LDS base + 16 L, so
+// the XOR swizzle of the LDS layout is applied on the global side by
+// choosing which 16-byte chunk each lane fetches.
 //
 // Pipeline: unit u of the K loop is A_t for u = 2t and B_t for u = 2t + 1;
 // it lives in ring slot u mod NU.  Step t computes two 32-deep sub-steps
@@ -220,7 +222,7 @@ __device__ __forceinline__ void gelu_tanh_staged(f32x4 (&v)[N]) {
 // fills unit row w R/4 + 8 q + L/8 at physical chunk L % 8, which must hold
 // logical chunk (L % 8) ^ key(row).  The source row is clamped to the last
 // of the operand's `rows` rows (r0 is the tile's first row, where the
-// buffer resource starts).
+// load's base points), so no load reads past the operand.
 template <int R, int LP>
 __device__ __forceinline__ void row_load_offsets(uint32_t (&v)[LP], int w, int lane, int64_t r0, int64_t rows,
                                                  int64_t ld) {
@@ -786,7 +788,7 @@ static CfgInfo cfg_info(int c) {
 
 // Whether the MFMA kernel can take a shape with a given tile: bf16 operands,
 // K a whole number of 64-wide steps, 16-byte aligned rows, one operand tile's
-// byte offsets below 2^31 (buffer offsets), and, with the LayerNorm
+// byte offsets below 2^31 (32-bit lane offsets), and, with the LayerNorm
 // epilogue, the column sums of Bop.  M and N may be ragged (row-major
 // operands only); N must be a multiple of 4 (the epilogue's quads).
 // K-major operands: Bop alone (store or GeLU-derivative epilogue) or both
@@ -802,7 +804,7 @@ static bool fits_cfg(const GemmArgs& g, int cfg) {
     const bool km = g.a_kmajor || g.b_kmajor;
     if (km && (ci.bm < 128 || ci.bn < 128 || g.M % ci.bm || g.N % ci.bn)) return false;
     if (g.lda % 8 || g.ldb % 8 || !aligned16(g.A) || !aligned16(g.B)) return false;
-    // buffer offsets: a tile's rows of a row-major operand, or all K rows of a K-major one
+    // 32-bit lane offsets: a tile's rows of a row-major operand, or all K rows of a K-major one
     if ((g.a_kmajor ? g.K : ci.bm) * g.lda * 2 >= ((int64_t)1 << 31)) return false;
     if ((g.b_kmajor ? g.K : ci.bn) * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
     if (g.a_kmajor && (!g.b_kmajor || g.epi != kEpiStore)) return false;
