@@ -264,8 +264,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // operands come in whole tiles.)
     const uint8_t* const pan_a = reinterpret_cast<const uint8_t*>(KA ? p.A + k0 * p.lda + m0 : p.A + m0 * p.lda + k0);
     const uint8_t* const pan_b = reinterpret_cast<const uint8_t*>(KB ? p.B + k0 * p.ldb + n0 : p.B + n0 * p.ldb + k0);
-    const uint64_t step_a = KA ? (uint64_t)BK * (uint64_t)p.lda * 2 : (uint64_t)BK * 2;
-    const uint64_t step_b = KB ? (uint64_t)BK * (uint64_t)p.ldb * 2 : (uint64_t)BK * 2;
+    // bytes per K step (below 2^31: a K-major operand's K rows are, see fits_cfg)
+    const uint32_t step_a = KA ? (uint32_t)(BK * p.lda * 2) : (uint32_t)(BK * 2);
+    const uint32_t step_b = KB ? (uint32_t)(BK * p.ldb * 2) : (uint32_t)(BK * 2);
     const int nk = kc / BK;   // >= 1
     // row-major operands: per-load lane offsets (rows clamped to the operand)
     uint32_t va[KA ? 1 : LPA], vb[KB ? 1 : LPB];
@@ -303,18 +304,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
     // the main loop)
     const uint32_t ring_lds = lds_addr(ring);
     auto load_one = [&](uint8_t* st, int op, int kstep, int q) {
-        const uint64_t ks = (uint64_t)(kstep < nk ? kstep : nk - 1);
+        const uint32_t ks = (uint32_t)(kstep < nk ? kstep : nk - 1);
         const uint32_t sl = ring_lds + (uint32_t)(st - ring);
         if (op) {
             uint32_t voff;
             if constexpr (KB) voff = kv_b[q];
             else voff = vb[q];
-            gdma16_asm(sl + dst_b + q * 1024, pan_b + ks * step_b, voff);
+            gdma16_asm(sl + dst_b + q * 1024, pan_b + (uint64_t)ks * step_b, voff);
         } else {
             uint32_t voff;
             if constexpr (KA) voff = kv_a[q];
             else voff = va[q];
-            gdma16_asm(sl + dst_a + q * 1024, pan_a + ks * step_a, voff);
+            gdma16_asm(sl + dst_a + q * 1024, pan_a + (uint64_t)ks * step_a, voff);
         }
     };
 
@@ -501,6 +502,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(FastParams p) {
                 step(ic<3>{}, tt);
                 if (++tt == nk - 1) break;
             }
+        }
+    } else if constexpr (NU == 5) {
+        // The other five-slot tiles carry the slots' LDS offsets instead: the
+        // five slots of step t + 1 are those of step t rotated, (A_t, B_t,
+        // A_t+1, B_t+1, P) -> (A_t+1, B_t+1, P, A_t, B_t), a few moves in
+        // place of the slot arithmetic.
+        uint32_t oa = 0, ob = SLOT, oa1 = 2 * SLOT, ob1 = 3 * SLOT, op = 4 * SLOT;
+        for (; tt < nk - 1; ++tt) {
+            const int u0 = 2 * tt + NU - 1;
+            sub_step(fa0, fb0, ring + oa, ring + ob, ch1, 1, fa1, fb1, true, ic<OP0>{}, ring + op, u0 >> 1);
+            barrier_wait(ic<C::VM_STEADY>{});
+            sub_step(fa1, fb1, ring + oa1, ring + ob1, ch0, 0, fa0, fb0, true, ic<OP1>{}, ring + oa, (u0 + 1) >> 1);
+            const uint32_t t0 = oa, t1 = ob;
+            oa = oa1;
+            ob = ob1;
+            oa1 = op;
+            ob1 = t0;
+            op = t1;
         }
     } else {
         int sa = 0;  // slot of A_t
