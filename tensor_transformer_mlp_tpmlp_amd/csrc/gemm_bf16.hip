@@ -810,8 +810,8 @@ static CfgInfo cfg_info(int c) {
 // byte offsets below 2^31 (32-bit lane offsets), and, with the LayerNorm
 // epilogue, the column sums of Bop.  M and N may be ragged (row-major
 // operands only); N must be a multiple of 4 (the epilogue's quads).
-// K-major operands: Bop alone (store or GeLU-derivative epilogue) or both
-// (store epilogue), without LayerNorm or the pre-activation stash, on whole
+// K-major operands: both at once (the backward's weight gradients), with
+// the store epilogue, without LayerNorm or the pre-activation stash, on whole
 // tiles of at least 128.  The GeLU output of the GeLU-derivative epilogue
 // goes with that epilogue only.
 static bool fits_cfg(const GemmArgs& g, int cfg) {
@@ -826,8 +826,8 @@ static bool fits_cfg(const GemmArgs& g, int cfg) {
     // 32-bit lane offsets: a tile's rows of a row-major operand, or all K rows of a K-major one
     if ((g.a_kmajor ? g.K : ci.bm) * g.lda * 2 >= ((int64_t)1 << 31)) return false;
     if ((g.b_kmajor ? g.K : ci.bn) * g.ldb * 2 >= ((int64_t)1 << 31)) return false;
-    if (g.a_kmajor && (!g.b_kmajor || g.epi != kEpiStore)) return false;
-    if (g.b_kmajor && ((g.epi != kEpiStore && g.epi != kEpiGeluGrad) || g.ln_mean || g.preact_out)) return false;
+    if (g.a_kmajor != g.b_kmajor) return false;
+    if (g.a_kmajor && (g.epi != kEpiStore || g.ln_mean || g.preact_out)) return false;
     const int64_t tiles = ((g.M + ci.bm - 1) / ci.bm) * ((g.N + ci.bn - 1) / ci.bn);
     if (tiles * 8 >= ((int64_t)1 << 31) || g.M >= ((int64_t)1 << 31) || g.N >= ((int64_t)1 << 31) ||
         g.K >= ((int64_t)1 << 31))
@@ -976,15 +976,11 @@ static hipError_t launch_store(const GemmArgs& g, int cfg, hipStream_t stream) {
                              : launch_typed<C, kEpiStore, bf16, KM>(g, 1, stream);
 }
 
-// K-major operands (fits_cfg admits Bop alone or both, with the store or
-// GeLU-derivative epilogue and no LayerNorm), on the two square tiles.
+// Both operands K-major (fits_cfg admits them with the store epilogue and
+// no LayerNorm), on the two square tiles.
 template <class C>
 static hipError_t launch_kmajor(const GemmArgs& g, int cfg, hipStream_t stream) {
-    if (g.a_kmajor) return launch_store<C, 3>(g, cfg, stream);
-    if (g.epi == kEpiGeluGrad)
-        return g.gelu_out ? launch_typed<C, kEpiGeluGradSave, bf16, 2>(g, 1, stream)
-                          : launch_typed<C, kEpiGeluGrad, bf16, 2>(g, 1, stream);
-    return launch_store<C, 2>(g, cfg, stream);
+    return launch_store<C, 3>(g, cfg, stream);
 }
 
 template <class C>
