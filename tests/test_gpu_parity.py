@@ -139,8 +139,8 @@ RING_SHAPES = [
     (4096, 192, 4096, 1),   # GEMM1 256x256, 3 steps
     (4096, 256, 4096, 2),   # GEMM1 256x256, 4 steps
     (4096, 320, 4096, 4),   # GEMM1 256x256, 5 steps
-    (4096, 384, 4096, 2),   # GEMM1 256x256, 6 steps (one full round of phases)
-    (4096, 448, 4096, 1),   # GEMM1 256x256, 7 steps (into the second round)
+    (4096, 384, 4096, 2),   # GEMM1 256x256, 6 steps (all five phases, then the exit)
+    (4096, 448, 4096, 1),   # GEMM1 256x256, 7 steps (the phases wrap around)
     (4096, 4096, 64, 1),    # GEMM2 256x256, 1 step
     (4096, 4096, 128, 1),   # GEMM2 256x256, 2 steps
     (4096, 4096, 192, 1),   # GEMM2 256x256, 3 steps
