@@ -202,7 +202,9 @@ def test_workload_large_sampled_rows(name):
     with NaN before the forward: every element of Y must then be finite
     (every output tile written, no stale H read), and one seeded row of
     every 256-row tile, plus the first and last rows, is compared with the
-    oracle (rows of Y depend only on the same rows of X)."""
+    oracle (rows of Y depend only on the same rows of X).  A second forward
+    into a fresh NaN-filled output must give the same Y bit for bit (no
+    race between tiles, at the size the bench times)."""
     w = workloads.WORKLOADS[name]
     say(f"{w.name}: {w.note} (NaN-poisoned Y and workspace, a row of every 256-row tile)")
     inp = workloads.make_inputs(w)
@@ -214,8 +216,12 @@ def test_workload_large_sampled_rows(name):
     ws.fill_(0xFF)  # NaN bit patterns everywhere in the workspace
     Y = torch.full((w.M, w.D), float("nan"), dtype=dt, device="cuda")
     tp.tp_mlp(X, sh, out=Y)
+    Y2 = torch.full_like(Y, float("nan"))
+    tp.tp_mlp(X, sh, out=Y2)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(Y).all()), "an element of Y was not written (or read a NaN)"
+    assert torch.equal(Y, Y2), "two forwards on the same inputs differ"
+    del Y2
     rows = sample_rows_per_tile(w.M, 256, seed=w.seed)
     assert len(rows) >= w.M // 256
     got = to_f64(Y[torch.from_numpy(rows).to(Y.device)])
