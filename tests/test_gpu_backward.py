@@ -85,11 +85,16 @@ def test_backward_h1024_full():
 
 def test_backward_headline_sampled():
     w = workloads.WORKLOADS["mlp_h4096_bf16"]
-    say(f"backward {w.name} (sampled rows of dX, columns of dA, rows of dB)")
+    say(f"backward {w.name} (twice; sampled rows of dX, columns of dA, rows of dB)")
     inp = workloads.make_inputs(w)
     dY = workloads.round_to_bf16(np.random.default_rng(w.seed + 7).standard_normal((w.M, w.D)).astype(np.float32))
     dX, dA, dB = _gpu_backward(inp, dY, w.n, "bf16")
     assert bool(torch.isfinite(dX).all()) and bool(torch.isfinite(dA).all()) and bool(torch.isfinite(dB).all())
+    # a second backward on the same inputs gives the same gradients bit for bit
+    again = _gpu_backward(inp, dY, w.n, "bf16")
+    for x, y, name in zip((dX, dA, dB), again, ("dX", "dA", "dB")):
+        assert torch.equal(x, y), f"two backwards differ in {name}"
+    del again
     rows = sample_rows(w.M, 16, seed=w.seed)
     rX, _, _ = oracle.tp_mlp_backward_full(inp.X[rows], inp.A, inp.B, w.n, dY[rows])
     assert_close(to_f64(dX[torch.from_numpy(rows).to(dX.device)]), rX, "bf16", f"dX rows {len(rows)}")
