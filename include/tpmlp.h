@@ -281,7 +281,8 @@ size_t tpmlp_backward_workspace_bytes(const tpmlp_shards* s, int64_t M);
  *   dA     device, D x F: dA_i in columns iF/n .. (i+1)F/n - 1 (A's layout).
  *   dB     device, F x D: dB_i in rows iF/n .. (i+1)F/n - 1 (B's layout).
  *   workspace  device, at least tpmlp_backward_workspace_bytes(s, M) bytes,
- *          16-byte aligned, caller-owned; contents are scratch.
+ *          16-byte aligned, caller-owned; contents are scratch.  That size
+ *          is 0 for M = 0, and the workspace may then be NULL.
  * Outputs must not overlap each other, the inputs or the workspace.
  * Errors: TPMLP_ERR_NULL, TPMLP_ERR_SHAPE (M < 0 or too large),
  * TPMLP_ERR_ALIGN, TPMLP_ERR_WORKSPACE, TPMLP_ERR_HIP; all but the last are

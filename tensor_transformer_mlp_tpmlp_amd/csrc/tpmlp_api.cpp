@@ -419,9 +419,9 @@ tpmlp_status tpmlp_backward(const void* X, const void* dY, int64_t M, const tpml
     if (!aligned16(dA) || !aligned16(dB) || (M > 0 && (!aligned16(X) || !aligned16(dY) || !aligned16(dX))) ||
         (preact && !aligned16(preact)) || (act && !aligned16(act)))
         return TPMLP_ERR_ALIGN;
-    const BwdLayout L = bwd_layout(s, M);
-    if (!workspace || workspace_bytes < L.total) return TPMLP_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return TPMLP_ERR_ALIGN;
+    const BwdLayout L = bwd_layout(s, M);  // 0 bytes for M = 0: the workspace may then be NULL
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return TPMLP_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return TPMLP_ERR_ALIGN;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int dt = s->dtype;

@@ -115,6 +115,15 @@ def test_backward_empty_batch_gives_zero_weight_grads():
     torch.cuda.synchronize()
     assert dX.shape == (0, 64)
     assert float(dA.float().abs().max()) == 0.0 and float(dB.float().abs().max()) == 0.0
+    # through the C ABI: an empty batch needs no workspace, so NULL is accepted
+    L = tp.lib()
+    assert L.tpmlp_backward_workspace_bytes(sh.handle, 0) == 0
+    dA2 = torch.full((64, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dB2 = torch.full((128, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    assert L.tpmlp_backward(None, None, 0, sh.handle, None, None, None, dA2.data_ptr(), dB2.data_ptr(),
+                            None, 0, None) == 0
+    torch.cuda.synchronize()
+    assert float(dA2.float().abs().max()) == 0.0 and float(dB2.float().abs().max()) == 0.0
 
 
 def test_backward_deterministic():

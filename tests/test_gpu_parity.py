@@ -146,6 +146,21 @@ RING_SHAPES = [
     (4096, 4096, 192, 1),   # GEMM2 256x256, 3 steps
     (4096, 4096, 448, 1),   # GEMM2 256x256, 7 steps
     (512, 192, 512, 2),     # GEMM1 128x128, 3 steps
+    # The ten-slot tiles run two loop bodies (fragment sets swapped) over a
+    # ring of five steps: step counts of either parity, each slot phase.
+    (512, 64, 512, 1),      # GEMM1 64x64, 1 step; GEMM2 64x64, 8 steps
+    (512, 128, 512, 1),     # GEMM1 64x64, 2 steps
+    (512, 512, 64, 1),      # GEMM2 64x64, 1 step
+    (512, 512, 192, 1),     # GEMM2 64x64, 3 steps
+    (512, 512, 256, 2),     # GEMM2 64x64, 4 steps
+    (512, 512, 320, 1),     # GEMM2 64x64, 5 steps
+    (512, 512, 384, 2),     # GEMM2 64x64, 6 steps
+    (512, 512, 704, 1),     # GEMM2 64x64, 11 steps
+    (2048, 1024, 64, 1),    # GEMM2 128x64, 1 step; GEMM1 64x64, 16 steps
+    (2048, 1024, 128, 2),   # GEMM2 128x64, 2 steps
+    (2048, 1024, 192, 1),   # GEMM2 128x64, 3 steps
+    (2048, 1024, 384, 2),   # GEMM2 128x64, 6 steps
+    (2048, 1024, 704, 1),   # GEMM1 128x64, 16 steps; GEMM2 128x64, 11 steps
 ]
 
 
