@@ -93,6 +93,10 @@ def test_shard_validation(L):
     assert _shard(L, D=0) == SHAPE
     assert _shard(L, F=-4) == SHAPE
     assert _shard(L, D=1 << 23) == SHAPE
+    assert _shard(L, D=(1 << 21) + 1) == SHAPE          # one past the largest dimension
+    assert _shard(L, D=1 << 21) == WS                   # the largest passes the shape check
+    assert _shard(L, F=(1 << 21) + 2, n=2) == SHAPE
+    assert _shard(L, F=1 << 21, n=2) == WS
     assert _shard(L, dt=2) == DTYPE
     assert _shard(L, A=None) == NULL
     assert _shard(L, B=None) == NULL

@@ -1,0 +1,84 @@
+"""Parity at the largest sizes the C ABI accepts: each of M, D and F at 2^21
+(the ABI's limit on a dimension), the others small, bf16.
+
+These stress what only the largest shapes reach: the tile counts and grid
+sizes of 2^21 rows or columns, the longest K loops (32768 steps of 64, with
+an fp32 accumulator over 2^21 terms), and the 64-bit panel offsets of tiles
+far into an operand.  The output and the workspace are filled with NaN first,
+so a tile that writes nothing, or a read of H that was never written, fails;
+the oracle checks one seeded row of every 256-row tile (rows of Y depend only
+on the same rows of X), or every row where M is small.  One more row than the
+limit is refused before any HIP call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import tensor_transformer_mlp_tpmlp_amd as tp
+from parity_util import (assert_close, oracle_forward, sample_rows_per_tile, say, to_dev, to_f64,
+                         workloads)
+
+pytestmark = pytest.mark.gpu
+
+MAX_DIM = 1 << 21
+SHAPE = 2  # TPMLP_ERR_SHAPE
+
+
+def _poisoned_forward(inp, n, **kw):
+    dt = torch.bfloat16
+    X, A, B = (to_dev(a, dt) for a in (inp.X, inp.A, inp.B))
+    sh = tp.shard_mlp(A, B, n)
+    M, D = X.shape
+    flags = 1 if kw.get("layernorm") else 0  # TPMLP_OPT_LAYERNORM
+    stream = torch.cuda.current_stream().cuda_stream
+    ws = sh.workspace(tp.lib().tpmlp_forward_workspace_bytes(sh.handle, M, flags, 0), stream)
+    ws.fill_(0xFF)  # NaN bit patterns everywhere in the workspace
+    Y = torch.full((M, D), float("nan"), dtype=dt, device="cuda")
+    if kw.pop("residual", False):
+        kw["residual"] = X
+    tp.tp_mlp(X, sh, out=Y, **kw)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Y).all()), "an element of Y was not written (or read a NaN)"
+    return Y, sh, X
+
+
+def test_max_rows():
+    """M = 2^21 rows (D = 64, F = 128): 2^21 / 128 row tiles on both GEMMs,
+    with and without the LayerNorm prologue and residual."""
+    M, D, F, n = MAX_DIM, 64, 128, 2
+    say(f"maximum M: M={M} D={D} F={F} n={n}")
+    inp = workloads.random_case(M, D, F, seed=2101, dtype="bf16")
+    rows = sample_rows_per_tile(M, 256, seed=2101)
+    idx = torch.from_numpy(rows).cuda()
+    Y, sh, X = _poisoned_forward(inp, n)
+    assert_close(to_f64(Y[idx]), oracle_forward(inp.X[rows], inp.A, inp.B, n), "bf16", f"M=2^21, rows {len(rows)}")
+    del Y
+    Yl, _, _ = _poisoned_forward(inp, n, layernorm=True, residual=True)
+    assert_close(to_f64(Yl[idx]), oracle_forward(inp.X[rows], inp.A, inp.B, n, layernorm=True, residual=True),
+                 "bf16", f"M=2^21 LN+residual, rows {len(rows)}")
+    del Yl
+    L = tp.lib()
+    assert L.tpmlp_forward_workspace_bytes(sh.handle, M + 1, 0, 0) == 0
+    Yd = torch.empty((1, D), dtype=torch.bfloat16, device="cuda")
+    assert L.tpmlp_forward_ex(X.data_ptr(), M + 1, sh.handle, Yd.data_ptr(), None, None) == SHAPE
+
+
+def test_max_hidden():
+    """D = 2^21 (M = 64, F = 64): GEMM1 runs a K loop of 2^21 / 64 = 32768
+    steps into one fp32 accumulator; GEMM2 has 2^21 output columns."""
+    M, D, F, n = 64, MAX_DIM, 64, 1
+    say(f"maximum D: M={M} D={D} F={F} n={n}")
+    inp = workloads.random_case(M, D, F, seed=2102, dtype="bf16")
+    Y, _, _ = _poisoned_forward(inp, n)
+    assert_close(to_f64(Y), oracle_forward(inp.X, inp.A, inp.B, n), "bf16", "D=2^21, every row")
+
+
+def test_max_intermediate():
+    """F = 2^21 over n = 2 shards (M = 64, D = 64): GEMM1 has 2^21 output
+    columns, and GEMM2's K loop sums both shards' 2^20 columns each, 32768
+    steps, in one fp32 accumulator."""
+    M, D, F, n = 64, 64, MAX_DIM, 2
+    say(f"maximum F: M={M} D={D} F={F} n={n}")
+    inp = workloads.random_case(M, D, F, seed=2103, dtype="bf16")
+    Y, _, _ = _poisoned_forward(inp, n)
+    assert_close(to_f64(Y), oracle_forward(inp.X, inp.A, inp.B, n), "bf16", "F=2^21, every row")
