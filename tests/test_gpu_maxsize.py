@@ -1,5 +1,6 @@
 """Parity at the largest sizes the C ABI accepts: each of M, D and F at 2^21
-(the ABI's limit on a dimension), the others small, bf16.
+(the ABI's limit on a dimension), the others small, bf16; and the backward
+over 2^21 rows.
 
 These stress what only the largest shapes reach: the tile counts and grid
 sizes of 2^21 rows or columns, the longest K loops (32768 steps of 64, with
@@ -14,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import tensor_transformer_mlp_tpmlp_amd as tp
 from parity_util import (assert_close, oracle_forward, sample_rows_per_tile, say, to_dev, to_f64,
                          workloads)
@@ -82,3 +84,25 @@ def test_max_intermediate():
     inp = workloads.random_case(M, D, F, seed=2103, dtype="bf16")
     Y, _, _ = _poisoned_forward(inp, n)
     assert_close(to_f64(Y), oracle_forward(inp.X, inp.A, inp.B, n), "bf16", "F=2^21, every row")
+
+
+def test_max_rows_backward():
+    """The backward over M = 2^21 rows (D = 128, F = 256, n = 2).  dA and dB
+    contract over the 2^21 rows: K-major K loops of 32768 steps, split into
+    ranges because their two output tiles leave the GPU almost empty (fp32
+    partials summed in range order)."""
+    M, D, F, n = MAX_DIM, 128, 256, 2
+    say(f"maximum M, backward: M={M} D={D} F={F} n={n}")
+    inp = workloads.random_case(M, D, F, seed=2104, dtype="bf16")
+    dY = workloads.round_to_bf16(np.random.default_rng(2105).standard_normal((M, D)).astype(np.float32))
+    dt = torch.bfloat16
+    X, A, B, tdY = (to_dev(a, dt) for a in (inp.X, inp.A, inp.B, dY))
+    sh = tp.shard_mlp(A, B, n)
+    dX, dA, dB = tp.tp_mlp_backward(X, tdY, sh)
+    torch.cuda.synchronize()
+    for t, name in ((dX, "dX"), (dA, "dA"), (dB, "dB")):
+        assert bool(torch.isfinite(t).all()), f"{name} has a non-finite element"
+    rX, rA, rB = oracle.tp_mlp_backward_full(inp.X, inp.A, inp.B, n, dY)
+    assert_close(to_f64(dA), rA, "bf16", "dA over 2^21 rows")
+    assert_close(to_f64(dB), rB, "bf16", "dB over 2^21 rows")
+    assert_close(to_f64(dX), rX, "bf16", "dX, every row")
