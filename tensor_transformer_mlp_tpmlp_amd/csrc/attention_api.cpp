@@ -150,7 +150,9 @@ tpmlp_status tpmlp_attn_pack(const void* Wq, const void* Wk, const void* Wv, con
 void tpmlp_attn_destroy(tpmlp_attn* a) { delete a; }
 
 size_t tpmlp_attn_workspace_bytes(const tpmlp_attn* a, int64_t batch, int64_t seq) {
+    // the sizes tpmlp_attention accepts, and no others
     if (!a || batch < 0 || seq < 0 || (seq > 0 && batch > kMaxTokens / seq) || seq > kMaxTokens) return 0;
+    if (batch > kMaxBatch || (seq > 0 && !attention_fits(seq, a->heads))) return 0;
     return ws_layout(a, batch * seq).total;
 }
 

@@ -1,6 +1,7 @@
 """Parity at the largest sizes the C ABI accepts: each of M, D and F at 2^21
-(the ABI's limit on a dimension), the others small, bf16; and the backward
-over 2^21 rows.
+(the ABI's limit on a dimension), the others small, bf16; the backward
+over 2^21 rows; and the attention half at its limits (one sequence of 2^21
+tokens, and 65535 sequences).
 
 These stress what only the largest shapes reach: the tile counts and grid
 sizes of 2^21 rows or columns, the longest K loops (32768 steps of 64, with
@@ -17,6 +18,7 @@ import torch
 
 import oracle
 import tensor_transformer_mlp_tpmlp_amd as tp
+from oracle import attention_oracle as ao
 from parity_util import (assert_close, oracle_forward, sample_rows_per_tile, say, to_dev, to_f64,
                          workloads)
 
@@ -106,3 +108,55 @@ def test_max_rows_backward():
     assert_close(to_f64(dA), rA, "bf16", "dA over 2^21 rows")
     assert_close(to_f64(dB), rB, "bf16", "dB over 2^21 rows")
     assert_close(to_f64(dX), rX, "bf16", "dX, every row")
+
+
+def _attn_weights(inp, heads, p):
+    dt = torch.bfloat16
+    x = to_dev(inp.x, dt)
+    aw = tp.shard_attention(to_dev(inp.Wq, dt), to_dev(inp.Wk, dt), to_dev(inp.Wv, dt), heads, p)
+    return x, aw
+
+
+def test_attention_longest_sequence():
+    """One sequence of 2^21 tokens (the token limit; one head of 64): every
+    query row's softmax runs over 32768 key tiles.  Query rows are
+    independent, so the oracle computes the sampled rows' attention over all
+    2^21 keys and values."""
+    seq, h = MAX_DIM, 64
+    say(f"attention: one sequence of {seq} tokens, one head")
+    inp = workloads.attn_case(1, seq, h, seed=2106)
+    x, aw = _attn_weights(inp, 1, 1)
+    out = tp.attention(x, 1, seq, aw, layernorm=False, residual=False)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    rows = sample_rows_per_tile(seq, seq // 16, seed=2106)
+    xs = inp.x.astype(np.float64)
+    ref = ao.head_attention(xs[rows] @ inp.Wq, xs @ inp.Wk, xs @ inp.Wv)
+    assert_close(to_f64(out[torch.from_numpy(rows).cuda()]), ref, "bf16", f"s=2^21, query rows {len(rows)}")
+
+
+def test_attention_most_sequences():
+    """65535 sequences (the batch limit, one grid dimension of the attention
+    kernel) of 32 tokens; a sample of sequences against the oracle, each
+    sequence on its own.  One more sequence is refused before any HIP call."""
+    batch, seq, h = 65535, 32, 64
+    say(f"attention: {batch} sequences of {seq} tokens, one head")
+    inp = workloads.attn_case(batch, seq, h, seed=2107)
+    x, aw = _attn_weights(inp, 1, 1)
+    out = tp.attention(x, batch, seq, aw, layernorm=False, residual=False)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    seqs = sample_rows_per_tile(batch, 2048, seed=2107)
+    got, ref = [], []
+    for b in seqs:
+        t = slice(b * seq, (b + 1) * seq)
+        xb = inp.x[t].astype(np.float64)
+        ref.append(ao.head_attention(xb @ inp.Wq, xb @ inp.Wk, xb @ inp.Wv))
+        got.append(to_f64(out[b * seq:(b + 1) * seq]))
+    assert_close(np.concatenate(got), np.concatenate(ref), "bf16", f"b=65535, sequences {len(seqs)}")
+    L = tp.lib()
+    assert L.tpmlp_attn_workspace_bytes(aw.handle, batch + 1, seq) == 0
+    nbytes = L.tpmlp_attn_workspace_bytes(aw.handle, batch, seq)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    assert L.tpmlp_attention(x.data_ptr(), batch + 1, seq, aw.handle, out.data_ptr(), 0, 0.0, ws.data_ptr(),
+                             nbytes, None, None) == SHAPE
