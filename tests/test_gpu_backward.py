@@ -251,3 +251,58 @@ def test_kept_activation_of_one_shard_and_alignment():
     o.workspace, o.workspace_bytes = ws.data_ptr(), ws.numel()
     o.save_act = H.data_ptr() + 4
     assert L.tpmlp_forward_ex(X.data_ptr(), M, sh.handle, Y.data_ptr(), ctypes.byref(o), None) == 6
+
+
+def _colwise_err(got, ref, axis):
+    """Largest normwise error over columns (axis 0) or rows (axis 1), each
+    scaled by its own max |ref|: columns of very different magnitude are
+    each checked at their own scale."""
+    scale = np.max(np.abs(ref), axis=axis)
+    err = np.max(np.abs(got - ref), axis=axis) / np.where(scale > 0, scale, 1.0)
+    return float(np.max(err))
+
+
+def test_gelu_saturation_forward_and_backward():
+    """GeLU and its derivative far into both tails, through the fused
+    epilogues: column j of A is scaled by 10^e_j, e_j cycling over -2 .. 29,
+    so S = X A reaches about 1e30 in magnitude (x^2 overflows fp32 inside
+    the GeLU, and the derivative's polynomial q overflows while s(1 - s) is
+    exactly 0).  GeLU(s) must tend to s and to 0, GeLU'(s) to 1 and to 0,
+    with no NaN; H is checked column by column and dB row by row at their
+    own scale, against the fp64 oracle."""
+    M, D, F, n = 128, 64, 256, 2
+    say(f"GeLU saturation, forward and backward, |S| up to ~1e30, M={M} D={D} F={F} n={n}")
+    inp, dY = _case(M, D, F, seed=4242, dtype="bf16")
+    scale = 10.0 ** (np.arange(F) % 32 - 2)
+    A = workloads.round_to_bf16((inp.A * scale[None, :]).astype(np.float32))
+    assert np.all(np.isfinite(A))
+    dt = torch.bfloat16
+    X, tA, B, tdY = (to_dev(a, dt) for a in (inp.X, A, inp.B, dY))
+    sh = tp.shard_mlp(tA, B, n)
+    S = torch.empty((M, F), dtype=dt, device="cuda")
+    H = torch.empty((M, F), dtype=dt, device="cuda")
+    Y = tp.tp_mlp(X, sh, save_preact=S, save_act=H)
+    Y0 = tp.tp_mlp(X, sh)  # the plain GeLU epilogue, keeping nothing
+    dX, dA, dB = tp.tp_mlp_backward(X, tdY, sh, preact=S, act=H)
+    dX2, dA2, dB2 = tp.tp_mlp_backward(X, tdY, sh)  # S and H recomputed
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y0)
+    for t, name in ((S, "S"), (H, "H"), (Y, "Y"), (dX, "dX"), (dA, "dA"), (dB, "dB")):
+        assert bool(torch.isfinite(t).all()), f"{name} has a non-finite element"
+    S_ref = inp.X.astype(np.float64) @ A.astype(np.float64)
+    assert float(np.max(np.abs(S_ref))) > 1e29
+    err_h = _colwise_err(to_f64(H), oracle.gelu(S_ref), axis=0)
+    say(f"H, column by column at its own scale: max error {err_h:.3e}")
+    assert err_h <= 1e-2
+    assert_close(to_f64(Y), oracle.tp_mlp(inp.X, oracle.shard_mlp(A, inp.B, n)), "bf16", "Y")
+    rX, rA, rB = oracle.tp_mlp_backward_full(inp.X, A, inp.B, n, dY)
+    assert_close(to_f64(dX), rX, "bf16", "dX")
+    err_a = _colwise_err(to_f64(dA), rA, axis=0)
+    err_b = _colwise_err(to_f64(dB), rB, axis=1)
+    say(f"dA column by column: {err_a:.3e}; dB row by row: {err_b:.3e}")
+    assert err_a <= 1e-2 and err_b <= 1e-2
+    # dX and dA do not read H: the same bits with S and H recomputed; dB uses
+    # the H recomputed from the rounded S, checked at its own scale
+    assert torch.equal(dX, dX2) and torch.equal(dA, dA2)
+    assert bool(torch.isfinite(dB2).all())
+    assert _colwise_err(to_f64(dB2), rB, axis=1) <= 1e-2
