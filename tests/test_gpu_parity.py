@@ -146,8 +146,9 @@ RING_SHAPES = [
     (4096, 4096, 192, 1),   # GEMM2 256x256, 3 steps
     (4096, 4096, 448, 1),   # GEMM2 256x256, 7 steps
     (512, 192, 512, 2),     # GEMM1 128x128, 3 steps
-    # The ten-slot tiles run two loop bodies (fragment sets swapped) over a
-    # ring of five steps: step counts of either parity, each slot phase.
+    # The ten-slot tiles (64x64, 128x64) run one loop body over ten slots
+    # (five steps of units, issued three steps ahead): short loops, and loops
+    # longer than the ring, whose slot index wraps.
     (512, 64, 512, 1),      # GEMM1 64x64, 1 step; GEMM2 64x64, 8 steps
     (512, 128, 512, 1),     # GEMM1 64x64, 2 steps
     (512, 512, 64, 1),      # GEMM2 64x64, 1 step
@@ -197,6 +198,29 @@ def test_layernorm_residual_shapes(M, D, F, n):
     assert_close(to_f64(Y), ref, "bf16", "LN+residual out")
     Yn, _, _ = _run(inp, n, "bf16", layernorm=True)
     assert_close(to_f64(Yn), oracle_forward(inp.X, inp.A, inp.B, n, layernorm=True), "bf16", "LN, no residual")
+
+
+@pytest.mark.parametrize("offset,spread", [(1024.0, 16.0), (8192.0, 16.0)])
+def test_layernorm_large_row_mean(offset, spread):
+    """Rows whose mean is large next to their spread (|mu| / sigma about 60
+    and about 500 after the bf16 rounding of x): the LayerNorm prologue's
+    correction r (x A - mu sum(A)) cancels most of x A, and the Norm after
+    the residual normalises an fp32 sum with the same offset.  Both must
+    still match the oracle, which normalises first, in fp64."""
+    M, D, F, n = 512, 1024, 2048, 4
+    say(f"LayerNorm, large row mean: offset {offset}, spread {spread}")
+    inp = workloads.random_case(M, D, F, seed=int(offset), dtype="bf16", sx=spread)
+    inp.X[:] = workloads.round_to_bf16(inp.X + np.float32(offset))
+    xs = inp.X.astype(np.float64)
+    say(f"row |mean| / std after rounding: {float(np.median(np.abs(xs.mean(1)) / xs.std(1))):.0f}")
+    Y, _, _ = _run(inp, n, "bf16", layernorm=True, residual=True)
+    assert_close(to_f64(Y), oracle_forward(inp.X, inp.A, inp.B, n, layernorm=True, residual=True), "bf16",
+                 "LN first + residual")
+    Yn, _, _ = _run(inp, n, "bf16", layernorm=True)
+    assert_close(to_f64(Yn), oracle_forward(inp.X, inp.A, inp.B, n, layernorm=True), "bf16", "LN first")
+    Ya, _, _ = _run(inp, n, "bf16", layernorm_after=True, residual=True)
+    assert_close(to_f64(Ya), oracle_forward(inp.X, inp.A, inp.B, n, residual=True, layernorm_after=True), "bf16",
+                 "Norm after the residual")
 
 
 # ---------------------------------------------------------------------------
